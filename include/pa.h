@@ -1,0 +1,196 @@
+/*
+ * pa.h -- C-ABI of libpa.so: attention over a paged KV cache on AMD MI355X
+ * (gfx950), as hand-written HIP kernels.
+ *
+ * Sources (web pages on the nano-vLLM teaching engine; titles abbreviated):
+ *   [Atlas]  "Visual atlas" figure index (diomchen.github.io/reference/visual-atlas)
+ *   [Course] "nano-vLLM offline" interactive course (3479845.xyz/nano-vllm)
+ *   [Guide]  "nano-vLLM interactive guide: 13 chapters" (blog-mushroom.pages.dev)
+ *   [Notes]  "Nano-vLLM reading notes, ch.1 overview" (wsj040303.github.io)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Element types.  q, k, v, pools and out are bf16 (IEEE-754 binary32 with the
+ *   low 16 bits dropped).  Index arrays are int32.  Arithmetic is fp32 with
+ *   bf16 MFMA inputs; outputs are rounded to bf16 (nearest, ties to even).
+ * Layouts (row-major, contiguous):
+ *   q, out            [tokens, num_q_heads, head_dim]
+ *   k, v              [tokens, num_kv_heads, head_dim]
+ *   k_cache, v_cache  [num_blocks, block_size, num_kv_heads, head_dim]; the pool
+ *                     row of slot s is element offset s * num_kv_heads * head_dim
+ *   block_tables      [num_seqs, max_blocks_per_seq]; entry [s][b] is the physical
+ *                     block holding sequence s's logical block b ([Course] "THE
+ *                     IMPORTANT DETAILS" item 02; [Atlas] ch.25 captions)
+ *   cu_seqlens_*      [num_seqs + 1] prefix sums of per-sequence lengths; sequence
+ *                     s owns rows cu[s] .. cu[s+1]-1 ([Atlas] figure index,
+ *                     flattening example cu_seqlens=[0,3,5])
+ * Memory.  Pointers marked (device) are HIP device pointers, (host) are host
+ *   pointers.  The caller owns every buffer: pools, metadata, workspace and
+ *   outputs.  The library allocates no device memory and never synchronises,
+ *   so every device entry point may be captured in a HIP graph; grid sizes
+ *   come only from the host integers passed in, never from device data.
+ * GQA.  Q head h reads KV head h / (num_q_heads / num_kv_heads): consecutive
+ *   Q heads form a group sharing one K/V head, with no physical copy ([Atlas]
+ *   figure index GQA example, ch.18 captions).
+ * Errors.  Host-checkable problems (NULL pointers, inconsistent or unsupported
+ *   sizes, a workspace too small) return a status before anything is launched.
+ *   Device-resident values (slots, tables, lengths) are not validated: values
+ *   outside the ranges stated below are undefined behaviour.  A failed launch
+ *   returns PA_ERR_LAUNCH.
+ * Threads.  No global state: entry points are re-entrant; calls on one stream
+ *   execute in order.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    PA_ERR_SHAPE = 2,       /* sizes negative, zero where not allowed, or
+                               inconsistent with each other                      */
+    PA_ERR_UNSUPPORTED = 3, /* valid sizes this build has no kernel for           */
+    PA_ERR_WORKSPACE = 4,   /* workspace_bytes smaller than required              */
+    PA_ERR_LAUNCH = 5       /* the HIP runtime reported a launch error            */
+} pa_status;
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char *pa_status_string(int status);
+
+/*
+ * Slot of every new token (host-side step metadata, as the model runner's
+ * prefill/decode preparation builds it: [Notes] "key state and module
+ * boundaries"; [Atlas] ch.29 captions).
+ *
+ * Sequence s has cu_seqlens_q[s+1] - cu_seqlens_q[s] new tokens, which are the
+ * last ones of its seqlens_k[s] tokens.  The token at logical position pos
+ * goes to
+ *     slot = block_tables[s][pos / block_size] * block_size + pos % block_size
+ * ([Atlas] figure index, slot example T=5, block_size=2, block_table=[3,0,4]).
+ *
+ * cu_seqlens_q  (host) [num_seqs+1], non-decreasing, cu_seqlens_q[0] == 0
+ * seqlens_k     (host) [num_seqs], seqlens_k[s] >= its new-token count
+ * block_tables  (host) [num_seqs, max_blocks_per_seq]
+ * slot_mapping  (host, out) [num_tokens], num_tokens == cu_seqlens_q[num_seqs]
+ * Returns PA_ERR_SHAPE if a position needs a table entry that is past
+ * max_blocks_per_seq or negative; slot_mapping is then left partly written.
+ */
+int pa_slot_mapping(const int32_t *cu_seqlens_q, const int32_t *seqlens_k, int32_t num_seqs,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    int32_t block_size, int32_t *slot_mapping, int32_t num_tokens);
+
+/*
+ * KV-cache store: for every token t with slot_mapping[t] >= 0,
+ *     k_cache row slot_mapping[t]  <-  k[t]      and the same for v,
+ * copied bit for bit ([Guide] ch.08 "attention and cache writes"; [Course]
+ * "ACCURACY & SCOPE": a token's K/V is written before sampling).  A negative
+ * slot marks a padding token and is skipped.
+ *
+ * k, v          (device) [num_tokens, num_kv_heads, head_dim] bf16
+ * k_cache/v_cache (device, in/out) [num_blocks, block_size, num_kv_heads, head_dim]
+ * slot_mapping  (device) [num_tokens]; each slot < num_blocks * block_size and
+ *               no two tokens share a slot
+ * num_tokens may be 0 (nothing is launched).  head_dim * num_kv_heads must be
+ * a multiple of 8.  k and v rows must not overlap the pools.
+ */
+int pa_store_kv(const void *k, const void *v, void *k_cache, void *v_cache,
+                const int32_t *slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                hipStream_t stream);
+
+/*
+ * Variable-length causal prefill attention.
+ *
+ * For sequence s: q_len = cu_seqlens_q[s+1] - cu_seqlens_q[s] query rows and
+ * k_len = cu_seqlens_k[s+1] - cu_seqlens_k[s] keys, q_len <= k_len.  The
+ * queries are the last q_len positions, so query row i (absolute position
+ * k_len - q_len + i) sees keys j <= k_len - q_len + i: the causal mask keeps
+ * the diagonal and, when a cached prefix precedes the chunk, is offset by the
+ * cached length ([Atlas] ch.17 captions; ch.26: after a prefix hit the query
+ * length differs from the key length).  With p_ij = exp(S_ij - max) over the
+ * visible keys, S_ij = scale * q_i . k_j, the output row is
+ * sum_j p_ij v_j / sum_j p_ij ([Atlas] ch.16 captions; figure index single-head
+ * causal example: first sum over d, second over Tk).
+ *
+ * Key source:
+ *   block_tables == NULL: keys are rows cu_seqlens_k[s] .. of flat k/v (no
+ *     cache); k_cache/v_cache are ignored and may be NULL.
+ *   block_tables != NULL: key j of sequence s is pool row
+ *     block_tables[s][j / block_size] * block_size + j % block_size; k/v are
+ *     ignored and may be NULL.  The chunk's own K/V must have been stored
+ *     (pa_store_kv) before this call.  Table entries past the last block a
+ *     sequence uses are never read.
+ *
+ * q        (device) [cu_seqlens_q[num_seqs], num_q_heads, head_dim] bf16
+ * out      (device, out) same shape as q, bf16; rows of every sequence written
+ * max_seqlen_q  >= every q_len (sizes the grid); max_seqlen_k >= every k_len
+ * max_blocks_per_seq  row length of block_tables (paged source only)
+ * block_size    any value >= 1 (paged source only)
+ * Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+int pa_prefill_varlen(const void *q, const void *k, const void *v,
+                      const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                      int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, void *out, hipStream_t stream);
+
+/*
+ * Number of key partitions pa_decode splits the longest context into, for
+ * the given partition_size (0 = the library's choice for these sizes).
+ * Returns 0 for invalid sizes.
+ */
+int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t partition_size);
+
+/*
+ * Bytes of device workspace pa_decode needs for these sizes (0 for invalid
+ * sizes).  The workspace holds one fp32 partial output row plus its running
+ * max and sum per (sequence, Q head, partition).
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len,
+                                int32_t partition_size);
+
+/*
+ * Paged decode attention: one new query per sequence over its whole history
+ * ([Atlas] ch.21 captions: a decode step's query attends over every cached
+ * token; the newest token's K/V is written first, so context_lens counts it).
+ *
+ * For sequence s and Q head h: keys j < context_lens[s], key j at pool row
+ * block_tables[s][j / block_size] * block_size + j % block_size; output
+ * sum_j p_j v_j / sum_j p_j with p_j = exp(scale q.k_j - max).
+ * The keys are split into partitions of partition_size tokens, each reduced
+ * to a partial (running max, sum, unnormalised output) in the workspace, and
+ * a second kernel combines the partials (log-sum-exp merge).  context_lens[s]
+ * == 0 yields a zero output row.
+ *
+ * q             (device) [num_seqs, num_q_heads, head_dim] bf16
+ * k_cache/v_cache (device) pools as above
+ * block_tables  (device) [num_seqs, max_blocks_per_seq]
+ * context_lens  (device) [num_seqs], 0 <= context_lens[s] <= max_context_len
+ * workspace     (device) >= pa_decode_workspace_size(...) bytes, any content
+ * out           (device, out) [num_seqs, num_q_heads, head_dim] bf16
+ * partition_size  0 (library's choice) or a multiple of 32 tokens
+ * Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ */
+int pa_decode(const void *q, const void *k_cache, const void *v_cache,
+              const int32_t *block_tables, int32_t max_blocks_per_seq,
+              const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+              int32_t block_size, float scale, int32_t partition_size,
+              void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,15 @@
+"""Paged KV attention for AMD MI355X (gfx950): KV-cache store, varlen causal
+prefill and split-K paged decode, as hand-written HIP kernels behind the C-ABI
+library ``libpa.so`` (declared in ``include/pa.h``).
+
+The Python names mirror the C entry points; they only marshal arguments
+(torch device tensors -> pointers, the current HIP stream) and raise when the
+library is missing or returns an error.  See ``binding.py``.
+"""
+from .binding import (PaError, library_path, load, pa_decode, pa_decode_workspace_size,  # noqa: F401
+                      pa_prefill_varlen, pa_slot_mapping, pa_status_string, pa_store_kv,
+                      pa_decode_num_partitions)
+
+__all__ = ["PaError", "library_path", "load", "pa_store_kv", "pa_prefill_varlen", "pa_decode",
+           "pa_decode_workspace_size", "pa_decode_num_partitions", "pa_slot_mapping",
+           "pa_status_string"]

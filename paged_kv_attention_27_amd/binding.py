@@ -1,0 +1,173 @@
+"""Thin ctypes binding of libpa.so (declared in include/pa.h).
+
+Each function has the name and argument order of its C entry point.  It only
+checks that tensors have the dtype, device and contiguity the C-ABI assumes,
+passes their data pointers and the current HIP stream, and raises ``PaError``
+on a non-zero status.  All computation happens in the library's HIP kernels;
+there is no fallback: if ``libpa.so`` is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+
+class PaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {pa_status_string(status)} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
+
+
+def load():
+    """Load libpa.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with "
+                           "`python -m paged_kv_attention_27_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_slot_mapping.restype = ctypes.c_int
+    lib.pa_slot_mapping.argtypes = [_P, _P, _I, _P, _I, _I, _P, _I]
+    lib.pa_store_kv.restype = ctypes.c_int
+    lib.pa_store_kv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+    lib.pa_prefill_varlen.restype = ctypes.c_int
+    lib.pa_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                      _I, _I, ctypes.c_float, _P, _P]
+    lib.pa_decode_num_partitions.restype = ctypes.c_int32
+    lib.pa_decode_num_partitions.argtypes = [_I, _I, _I, _I]
+    lib.pa_decode_workspace_size.restype = ctypes.c_size_t
+    lib.pa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                              _I, _P, _SZ, _P, _P]
+    _LIB = lib
+    return lib
+
+
+def pa_status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise PaError(fn, status)
+
+
+def _dev(t, dtype, name, optional=False):
+    if t is None:
+        if optional:
+            return None
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda \
+            or not t.is_contiguous():
+        raise TypeError(f"{name}: expected a contiguous {dtype} tensor on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def pa_slot_mapping(cu_seqlens_q, seqlens_k, block_tables, block_size):
+    """Host-side slot of every new token (int32 CPU tensors in, int32 CPU tensor out)."""
+    cu = torch.as_tensor(cu_seqlens_q, dtype=torch.int32).contiguous()
+    sk = torch.as_tensor(seqlens_k, dtype=torch.int32).contiguous()
+    bt = torch.as_tensor(block_tables, dtype=torch.int32).contiguous()
+    n = int(cu[-1])
+    out = torch.empty(n, dtype=torch.int32)
+    st = load().pa_slot_mapping(cu.data_ptr(), sk.data_ptr(), cu.numel() - 1, bt.data_ptr(),
+                                bt.shape[1], int(block_size), out.data_ptr(), n)
+    _check("pa_slot_mapping", st)
+    return out
+
+
+def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
+    T, Hkv, d = k.shape
+    NB, bs = k_cache.shape[0], k_cache.shape[1]
+    if tuple(v.shape) != tuple(k.shape) or tuple(k_cache.shape) != (NB, bs, Hkv, d) \
+            or tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("pa_store_kv: inconsistent shapes")
+    st = load().pa_store_kv(_dev(k, torch.bfloat16, "k"), _dev(v, torch.bfloat16, "v"),
+                            _dev(k_cache, torch.bfloat16, "k_cache"),
+                            _dev(v_cache, torch.bfloat16, "v_cache"),
+                            _dev(slot_mapping, torch.int32, "slot_mapping"),
+                            T, NB, bs, Hkv, d, _stream(stream))
+    _check("pa_store_kv", st)
+
+
+def pa_prefill_varlen(q, k, v, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
+                      max_seqlen_q, max_seqlen_k, num_kv_heads, scale, out=None,
+                      block_size=None, stream=None):
+    Tq, Hq, d = q.shape
+    num_seqs = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty_like(q)
+    paged = block_tables is not None
+    if paged:
+        bs = k_cache.shape[1] if block_size is None else block_size
+        maxb = block_tables.shape[1]
+    else:
+        bs, maxb = (1 if block_size is None else block_size), 0
+    st = load().pa_prefill_varlen(
+        _dev(q, torch.bfloat16, "q"),
+        _dev(k, torch.bfloat16, "k", optional=True),
+        _dev(v, torch.bfloat16, "v", optional=True),
+        _dev(k_cache, torch.bfloat16, "k_cache", optional=True),
+        _dev(v_cache, torch.bfloat16, "v_cache", optional=True),
+        _dev(block_tables, torch.int32, "block_tables", optional=True), maxb,
+        _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q"),
+        _dev(cu_seqlens_k, torch.int32, "cu_seqlens_k"),
+        num_seqs, int(max_seqlen_q), int(max_seqlen_k), Hq, int(num_kv_heads), d, int(bs),
+        float(scale), _dev(out, torch.bfloat16, "out"), _stream(stream))
+    _check("pa_prefill_varlen", st)
+    return out
+
+
+def pa_decode_num_partitions(num_seqs, num_kv_heads, max_context_len, partition_size=0):
+    return int(load().pa_decode_num_partitions(num_seqs, num_kv_heads, max_context_len,
+                                               partition_size))
+
+
+def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                             partition_size=0):
+    return int(load().pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                               max_context_len, partition_size))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+              workspace=None, out=None, partition_size=0, stream=None):
+    S, Hq, d = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load().pa_decode(
+        _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens"), S, int(max_context_len), Hq, Hkv, d,
+        bs, float(scale), int(partition_size), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _dev(out, torch.bfloat16, "out"), _stream(stream))
+    _check("pa_decode", st)
+    return out
