@@ -189,6 +189,28 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               int32_t block_size, float scale, int32_t partition_size,
               void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
 
+/*
+ * The two passes of pa_decode, for callers that schedule or time them apart.
+ * Arguments are those of pa_decode.  pa_decode_split runs the partition pass:
+ * it writes the final output row of every sequence whose context fits in one
+ * partition, and the partials of the others into the workspace.
+ * pa_decode_reduce then merges the partials (and writes the zero rows of empty
+ * contexts).  Calling pa_decode_split and then pa_decode_reduce on one stream
+ * with the same arguments is exactly pa_decode.
+ */
+int pa_decode_split(const void *q, const void *k_cache, const void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, int32_t partition_size,
+                    void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
+int pa_decode_reduce(const void *q, const void *k_cache, const void *v_cache,
+                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                     const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                     int32_t block_size, float scale, int32_t partition_size,
+                     void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

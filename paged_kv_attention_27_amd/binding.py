@@ -54,9 +54,11 @@ def load():
     lib.pa_decode_num_partitions.argtypes = [_I, _I, _I, _I]
     lib.pa_decode_workspace_size.restype = ctypes.c_size_t
     lib.pa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
-    lib.pa_decode.restype = ctypes.c_int
-    lib.pa_decode.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
-                              _I, _P, _SZ, _P, _P]
+    for name in ("pa_decode", "pa_decode_split", "pa_decode_reduce"):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
+                       _I, _P, _SZ, _P, _P]
     _LIB = lib
     return lib
 
@@ -154,7 +156,7 @@ def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-              workspace=None, out=None, partition_size=0, stream=None):
+              workspace=None, out=None, partition_size=0, stream=None, _entry="pa_decode"):
     S, Hq, d = q.shape
     NB, bs, Hkv, _ = k_cache.shape
     if out is None:
@@ -162,12 +164,26 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
     need = pa_decode_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    st = load().pa_decode(
+    st = getattr(load(), _entry)(
         _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
         _dev(v_cache, torch.bfloat16, "v_cache"),
         _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
         _dev(context_lens, torch.int32, "context_lens"), S, int(max_context_len), Hq, Hkv, d,
         bs, float(scale), int(partition_size), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(out, torch.bfloat16, "out"), _stream(stream))
-    _check("pa_decode", st)
+    _check(_entry, st)
     return out
+
+
+def pa_decode_split(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                    workspace, out, partition_size=0, stream=None):
+    """Partition pass of pa_decode (same arguments); see include/pa.h."""
+    return pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                     workspace, out, partition_size, stream, _entry="pa_decode_split")
+
+
+def pa_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                     workspace, out, partition_size=0, stream=None):
+    """Reduce pass of pa_decode (same arguments); see include/pa.h."""
+    return pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                     workspace, out, partition_size, stream, _entry="pa_decode_reduce")

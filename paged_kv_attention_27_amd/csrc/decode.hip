@@ -1,0 +1,275 @@
+// decode.hip -- paged decode attention: one new query per sequence attends
+// over its whole history through its block table ("Visual atlas" ch.21
+// captions: one decode step; "nano-vLLM offline" course, THE IMPORTANT
+// DETAILS item 02: logical blocks map to non-contiguous physical blocks).
+//
+// Memory-bound split-K design for gfx950:
+//   * decode_split_kernel: one workgroup per (partition of part_tokens keys,
+//     KV head, sequence).  The g = Hq/Hkv query heads of the group share every
+//     K/V row the workgroup loads (GQA without a physical repeat, "Visual
+//     atlas" ch.18).  A token's 256-byte K row is read by 16 lanes x 16 bytes,
+//     so each wave64 load instruction moves four whole rows; every wave keeps
+//     U rows of K and of V per lane group in flight at once.  Dot products use
+//     v_dot2_f32_bf16 and a 4-step DPP row reduction; the softmax runs online
+//     in the log2 domain (scale * log2 e folded into the scores).  Each wave
+//     keeps its own running max/sum/output; the four waves are merged in LDS.
+//   * If a sequence fits in one partition, that workgroup writes the final
+//     bf16 output; otherwise it writes the partition's running max, sum and
+//     unnormalised output row (fp32) to the workspace and
+//   * decode_reduce_kernel merges a sequence's partitions with the usual
+//     log-sum-exp rescaling: M = max m_p, L = sum 2^(m_p - M) l_p,
+//     o = sum 2^(m_p - M) o_p / L.
+// Keys at or past context_lens[s] are never loaded, so stale pool slots
+// (a free block is not cleared, "Visual atlas" ch.25) cannot reach the output.
+#include "pa_common.h"
+
+namespace pa {
+namespace {
+
+constexpr int D = 128;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kTableCache = 1024;
+
+__device__ __forceinline__ int block_of(int j, int bs, int shift) {
+    return shift >= 0 ? (j >> shift) : (j / bs);
+}
+
+template <int G, int U>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
+{
+    const int p = blockIdx.x;
+    const int kvh = blockIdx.y;
+    const int s = blockIdx.z;
+    const int ctx = a.context_lens[s];
+    const int P = a.part_tokens;
+    const int t_begin = p * P;
+    if (t_begin >= ctx)
+        return;
+    const int t_end = min(ctx, t_begin + P);
+    const int n_part_s = (ctx + P - 1) / P;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int r = lane >> 4;   // lane group: which of the four rows a load instruction covers
+    const int c = lane & 15;   // 8-element slice of the head dimension
+
+    __shared__ int32_t tbl[kTableCache];
+    __shared__ float red_m[kWaves][G];
+    __shared__ float red_l[kWaves][G];
+    __shared__ float red_o[kWaves][G][D];
+
+    const int bs = a.block_size, shift = a.bs_shift;
+    const int blk_first = block_of(t_begin, bs, shift);
+    const int blk_last = block_of(t_end - 1, bs, shift);
+    const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
+    for (int i = tid; i <= blk_last - blk_first; i += kThreads)
+        tbl[i] = bt_row[blk_first + i];
+
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    const bf16 *q = static_cast<const bf16 *>(a.q);
+    uint32_t qw[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)s * Hq + kvh * G + h) * D + 8 * c);
+        qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
+    }
+    __syncthreads();
+
+    float m[G], l[G], acc[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        m[h] = kMaxFloor;
+        l[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    }
+
+    const bf16 *kc = static_cast<const bf16 *>(a.k_cache);
+    const bf16 *vc = static_cast<const bf16 *>(a.v_cache);
+    const float sl2 = a.scale_log2;
+    constexpr int kChunk = 4 * U;   // keys per wave iteration
+    const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
+
+    for (int ch = wave; ch < n_chunks; ch += kWaves) {
+        const int base = t_begin + ch * kChunk + r * U;
+        uint4 kr[U], vr[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int j = base + u;
+            if (j < t_end) {
+                const int lb = block_of(j, bs, shift);
+                const int64_t row = (int64_t)tbl[lb - blk_first] * bs + (j - lb * bs);
+                const int64_t off = (row * Hkv + kvh) * D + 8 * c;
+                kr[u] = *reinterpret_cast<const uint4 *>(kc + off);
+                vr[u] = *reinterpret_cast<const uint4 *>(vc + off);
+            } else {
+                kr[u] = make_uint4(0, 0, 0, 0);
+                vr[u] = make_uint4(0, 0, 0, 0);
+            }
+        }
+
+        float sc[G][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool valid = base + u < t_end;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d0 = 0.f;
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][0]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].x), d0, false);
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][1]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].y), d0, false);
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][2]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].z), d0, false);
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][3]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].w), d0, false);
+                const float dot = row16_sum(d0);
+                sc[h][u] = valid ? dot * sl2 : -INFINITY;
+            }
+        }
+
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float mx = sc[h][0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[h][u]);
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            const float mnew = fmaxf(m[h], mx);
+            const float alpha = fast_exp2(m[h] - mnew);
+            m[h] = mnew;
+            l[h] *= alpha;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+        }
+
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float vf[8];
+            vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
+            vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
+            vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
+            vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float pw = fast_exp2(sc[h][u] - m[h]);
+                l[h] += pw;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw, vf[e], acc[h][e]);
+            }
+        }
+    }
+
+    // merge the four lane groups of the wave (they share the running max)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        l[h] += shfl_xor_f(l[h], 16);
+        l[h] += shfl_xor_f(l[h], 32);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            acc[h][e] += shfl_xor_f(acc[h][e], 16);
+            acc[h][e] += shfl_xor_f(acc[h][e], 32);
+        }
+    }
+    if (r == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red_o[wave][h][8 * c + e] = acc[h][e];
+            if (c == 0) {
+                red_m[wave][h] = m[h];
+                red_l[wave][h] = l[h];
+            }
+        }
+    }
+    __syncthreads();
+
+    // merge the waves and emit the partition's result
+    for (int idx = tid; idx < G * D; idx += kThreads) {
+        const int h = idx / D, dd = idx % D;
+        float M = red_m[0][h];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, red_m[w][h]);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(red_m[w][h] - M);
+            L = fmaf(f, red_l[w][h], L);
+            o = fmaf(f, red_o[w][h][dd], o);
+        }
+        const int head = kvh * G + h;
+        if (n_part_s == 1) {
+            uint16_t *out = static_cast<uint16_t *>(a.out);
+            out[((int64_t)s * Hq + head) * D + dd] = f32_to_bf16_bits(o / L);
+        } else {
+            const int64_t slot = ((int64_t)s * Hq + head) * a.n_part + p;
+            a.ws_o[slot * D + dd] = o;
+            if (dd == 0) {
+                a.ws_ml[slot * 2 + 0] = M;
+                a.ws_ml[slot * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a)
+{
+    const int h = blockIdx.x;
+    const int s = blockIdx.y;
+    const int dd = threadIdx.x;
+    const int ctx = a.context_lens[s];
+    const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
+    if (np == 1)
+        return;  // the single partition wrote the output itself
+    uint16_t *out = static_cast<uint16_t *>(a.out) + ((int64_t)s * a.num_q_heads + h) * D + dd;
+    if (np <= 0) {
+        *out = 0;  // empty context: defined as a zero row
+        return;
+    }
+    const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.n_part;
+    const float *ml = a.ws_ml + base * 2;
+    float M = kMaxFloor;
+    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+    float L = 0.f, o = 0.f;
+    for (int p = 0; p < np; ++p) {
+        const float f = fast_exp2(ml[2 * p] - M);
+        L = fmaf(f, ml[2 * p + 1], L);
+        o = fmaf(f, a.ws_o[(base + p) * D + dd], o);
+    }
+    *out = f32_to_bf16_bits(o / L);
+}
+
+template <int G, int U>
+hipError_t launch_g(const DecodeArgs &a, int passes, hipStream_t stream)
+{
+    if (passes & 1) {
+        dim3 grid(a.n_part, a.num_kv_heads, a.num_seqs);
+        hipLaunchKernelGGL((decode_split_kernel<G, U>), grid, dim3(kThreads), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    if (passes & 2) {
+        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.num_q_heads, a.num_seqs), dim3(D), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, int passes, hipStream_t stream)
+{
+    switch (a.num_q_heads / a.num_kv_heads) {
+    case 1: return launch_g<1, 8>(a, passes, stream);
+    case 2: return launch_g<2, 8>(a, passes, stream);
+    case 4: return launch_g<4, 8>(a, passes, stream);
+    case 8: return launch_g<8, 4>(a, passes, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace pa

@@ -1,0 +1,105 @@
+// pa_common.h -- device helpers and launcher declarations shared by the HIP
+// kernels of libpa.so (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+// Running-max floor: finite, so an all-masked row gives exp2(floor - floor) = 1
+// for the rescale factor and exp2(-inf - floor) = 0 for every weight.
+constexpr float kMaxFloor = -3.0e38f;
+
+// bf16 pair packed in a 32-bit word -> two fp32 values (exact widening).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (bf16)x);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row receives the same
+// bit-exact total (each step adds a value to its mirror, which commutes).
+__device__ __forceinline__ float row16_sum(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0xB1, 0xF, 0xF, false)); // quad_perm [1,0,3,2]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x4E, 0xF, 0xF, false)); // quad_perm [2,3,0,1]
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x141, 0xF, 0xF, false)); // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               0x140, 0xF, 0xF, false)); // row_mirror
+    return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error; arguments are pre-validated.
+
+hipError_t launch_store_kv(const void *k, const void *v, void *k_cache, void *v_cache,
+                           const int32_t *slot_mapping, int32_t num_tokens,
+                           int32_t row_elems, hipStream_t stream);
+
+struct DecodeArgs {
+    const void *q;
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *context_lens;
+    void *out;
+    float *ws_o;      // [S, Hq, n_part, head_dim] unnormalised partial outputs
+    float *ws_ml;     // [S, Hq, n_part, 2] running max (log2 domain) and sum
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t bs_shift;   // log2(block_size) if a power of two, else -1
+    int32_t part_tokens;
+    int32_t n_part;
+    float scale_log2;   // scale * log2(e)
+};
+// passes: bit 0 = partition (split) pass, bit 1 = reduce pass
+hipError_t launch_decode(const DecodeArgs &a, int passes, hipStream_t stream);
+
+struct PrefillArgs {
+    const void *q;
+    const void *k;        // flat source (paged == false)
+    const void *v;
+    const void *k_cache;  // paged source (paged == true)
+    const void *v_cache;
+    const int32_t *block_tables;
+    const int32_t *cu_seqlens_q;
+    const int32_t *cu_seqlens_k;
+    void *out;
+    int32_t max_blocks;
+    int32_t num_seqs;
+    int32_t max_seqlen_q;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t block_size;
+    int32_t bs_shift;
+    bool paged;
+    float scale_log2;
+};
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+}  // namespace pa

@@ -146,12 +146,15 @@ def _nan_pool(nb, bs, hkv, d):
     return np.full((nb, bs, hkv, d), BF16_NAN, dtype=np.uint16)
 
 
-def _phase(rng, lengths, seqlens_k, Hq, Hkv, d, paged) -> Phase:
+def _phase(rng, lengths, seqlens_k, Hq, Hkv, d, paged, values=True) -> Phase:
     lengths = np.asarray(lengths, dtype=np.int64)
     T = int(lengths.sum())
-    q = normal_bf16(rng, (T, Hq, d))
-    k = normal_bf16(rng, (T, Hkv, d))
-    v = normal_bf16(rng, (T, Hkv, d))
+    if values:
+        q = normal_bf16(rng, (T, Hq, d))
+        k = normal_bf16(rng, (T, Hkv, d))
+        v = normal_bf16(rng, (T, Hkv, d))
+    else:
+        q = k = v = None
     cu = _cu(lengths)
     sk = np.asarray(seqlens_k, dtype=np.int32)
     return Phase(q=q, k=k, v=v, cu_seqlens_q=cu, seqlens_k=sk, paged=paged,
@@ -164,16 +167,26 @@ def _blocks_for(n_tokens: int, bs: int) -> int:
     return -(-int(n_tokens) // bs)
 
 
-def config1(seed: int = 27001) -> Workload:
+def _streams(seed: int):
+    """Independent generators: metadata, pools, prefill, prefix, decode values.
+
+    Each component has a stream of its own, so drawing (or skipping) one never
+    shifts another.
+    """
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(5)]
+
+
+def config1(seed: int = 27001, values: bool = True) -> Workload:
     """4 sequences {17,256,300,511}: full causal prefill, then one decode step."""
-    rng = np.random.default_rng(seed)
+    meta, _, r_pre, _, r_dec = _streams(seed)
     Hq, Hkv, d, bs, NB = 16, 8, 128, 256, 16
     L = np.array([17, 256, 300, 511])
-    perm = rng.permutation(NB).astype(np.int32)
+    perm = meta.permutation(NB).astype(np.int32)
     nb = [_blocks_for(n + 1, bs) for n in L]  # room for the decode token
     bt = _tables(perm, nb, max(nb))
-    prefill = _phase(rng, L, L, Hq, Hkv, d, paged=False)
-    decode = _phase(rng, np.ones(len(L), np.int64), L + 1, Hq, Hkv, d, paged=True)
+    prefill = _phase(r_pre, L, L, Hq, Hkv, d, paged=False, values=values)
+    decode = _phase(r_dec, np.ones(len(L), np.int64), L + 1, Hq, Hkv, d, paged=True,
+                    values=values)
     return Workload("c1_tiny_prefill_decode",
                     "4 seqs L={17,256,300,511}, Hq16/Hkv8/d128, bs256, 16-block pool; "
                     "store+prefill then one decode step",
@@ -181,15 +194,15 @@ def config1(seed: int = 27001) -> Workload:
                     _nan_pool(NB, bs, Hkv, d), prefill=prefill, decode=decode)
 
 
-def config2(seed: int = 27002) -> Workload:
+def config2(seed: int = 27002, values: bool = True) -> Workload:
     """8 sequences, lengths U[100,1024], varlen causal prefill from flat K/V."""
-    rng = np.random.default_rng(seed)
+    meta, _, r_pre, _, _ = _streams(seed)
     Hq, Hkv, d, bs, NB = 16, 8, 128, 256, 64
-    L = rng.integers(100, 1024, size=8, endpoint=True)
-    perm = rng.permutation(NB).astype(np.int32)
+    L = meta.integers(100, 1024, size=8, endpoint=True)
+    perm = meta.permutation(NB).astype(np.int32)
     nb = [_blocks_for(n, bs) for n in L]
     bt = _tables(perm, nb, max(nb))
-    prefill = _phase(rng, L, L, Hq, Hkv, d, paged=False)
+    prefill = _phase(r_pre, L, L, Hq, Hkv, d, paged=False, values=values)
     return Workload("c2_varlen_prefill",
                     "8 seqs L~U[100,1024], Hq16/Hkv8/d128, bs256, store into 64-block pool; "
                     "causal prefill from flat K/V",
@@ -197,19 +210,19 @@ def config2(seed: int = 27002) -> Workload:
                     _nan_pool(NB, bs, Hkv, d), prefill=prefill)
 
 
-def config3(seed: int = 27003) -> Workload:
+def config3(seed: int = 27003, values: bool = True) -> Workload:
     """16 sequences share a 512-token cached prefix; chunks U[64,1024] attend to it."""
-    rng = np.random.default_rng(seed)
+    meta, _, r_pre, r_fix, _ = _streams(seed)
     Hq, Hkv, d, bs, NB, P = 16, 8, 128, 256, 128, 512
-    Lq = rng.integers(64, 1024, size=16, endpoint=True)
-    perm = rng.permutation(NB).astype(np.int32)
+    Lq = meta.integers(64, 1024, size=16, endpoint=True)
+    perm = meta.permutation(NB).astype(np.int32)
     n_shared = P // bs
     shared = perm[:n_shared]
     nb = [_blocks_for(P + n, bs) - n_shared for n in Lq]
     bt = _tables(perm[n_shared:], nb, n_shared + max(nb), shared=shared)
-    prefill = _phase(rng, Lq, P + Lq, Hq, Hkv, d, paged=True)
+    prefill = _phase(r_pre, Lq, P + Lq, Hq, Hkv, d, paged=True, values=values)
     # the prefix is written once, as the first P positions of sequence 0
-    prefix = _phase(rng, [P], [P], Hq, Hkv, d, paged=True)
+    prefix = _phase(r_fix, [P], [P], Hq, Hkv, d, paged=True, values=values)
     return Workload("c3_prefix_chunked_prefill",
                     "16 seqs, shared 512-token cached prefix (2 shared blocks) + chunk "
                     "q~U[64,1024]; Hq16/Hkv8/d128, bs256, 128-block pool; prefill reads pools",
@@ -223,7 +236,7 @@ def _history_pools(rng, bt, NB, bs, Hkv, d):
     used = np.unique(bt[bt >= 0])
     kc = _nan_pool(NB, bs, Hkv, d)
     vc = _nan_pool(NB, bs, Hkv, d)
-    # draw block by block in table order so the content does not depend on NB
+    # used blocks in ascending physical id, K first, then V
     kvals = normal_bf16(rng, (len(used), bs, Hkv, d))
     vvals = normal_bf16(rng, (len(used), bs, Hkv, d))
     kc[used] = kvals
@@ -231,33 +244,38 @@ def _history_pools(rng, bt, NB, bs, Hkv, d):
     return kc, vc
 
 
-def _decode_config(name, desc, rng, S, ctx, Hq, Hkv, d, bs, NB) -> Workload:
-    perm = rng.permutation(NB).astype(np.int32)
+def _decode_config(name, desc, streams, ctx, Hq, Hkv, d, bs, NB, values) -> Workload:
+    meta, r_pool, _, _, r_dec = streams
+    S = len(ctx)
+    perm = meta.permutation(NB).astype(np.int32)
     nb = [_blocks_for(c, bs) for c in ctx]
     bt = _tables(perm, nb, max(nb))
-    kc, vc = _history_pools(rng, bt, NB, bs, Hkv, d)
-    decode = _phase(rng, np.ones(S, np.int64), ctx, Hq, Hkv, d, paged=True)
+    if values:
+        kc, vc = _history_pools(r_pool, bt, NB, bs, Hkv, d)
+    else:
+        kc = vc = None
+    decode = _phase(r_dec, np.ones(S, np.int64), ctx, Hq, Hkv, d, paged=True, values=values)
     return Workload(name, desc, Hq, Hkv, d, bs, NB, _scale(d), bt, kc, vc, decode=decode)
 
 
-def config4(seed: int = 27004) -> Workload:
+def config4(seed: int = 27004, values: bool = True) -> Workload:
     """256 sequences decode, context U[128,4096] (new token included)."""
-    rng = np.random.default_rng(seed)
-    ctx = rng.integers(128, 4096, size=256, endpoint=True).astype(np.int32)
+    streams = _streams(seed)
+    ctx = streams[0].integers(128, 4096, size=256, endpoint=True).astype(np.int32)
     return _decode_config("c4_batched_decode",
                           "256 seqs, ctx~U[128,4096] incl. new token, Hq16/Hkv8/d128, bs256, "
                           "4096-block pool; store new K/V then paged decode",
-                          rng, 256, ctx, 16, 8, 128, 256, 4096)
+                          streams, ctx, 16, 8, 128, 256, 4096, values)
 
 
-def config5(seed: int = 27005) -> Workload:
+def config5(seed: int = 27005, values: bool = True) -> Workload:
     """16 sequences x 32768 context, Hq=32 over Hkv=8 (group of 4)."""
-    rng = np.random.default_rng(seed)
+    streams = _streams(seed)
     ctx = np.full(16, 32768, dtype=np.int32)
     return _decode_config("c5_long_decode",
                           "16 seqs x ctx 32768, Hq32/Hkv8/d128, bs256, 2048-block pool; "
                           "store new K/V then split-K paged decode",
-                          rng, 16, ctx, 32, 8, 128, 256, 2048)
+                          streams, ctx, 32, 8, 128, 256, 2048, values)
 
 
 def _scale(d: int) -> float:
@@ -268,5 +286,55 @@ def _scale(d: int) -> float:
 CONFIGS = {1: config1, 2: config2, 3: config3, 4: config4, 5: config5}
 
 
-def make(cfg_id: int) -> Workload:
-    return CONFIGS[cfg_id]()
+def make(cfg_id: int, values: bool = True) -> Workload:
+    """Workload of config 1..5; values=False draws only lengths and tables."""
+    return CONFIGS[cfg_id](values=values)
+
+
+def synthetic(q_lens, k_lens, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+              seed=0, paged=True, q_scale=1.0, q_zero=False, v_position=False,
+              extra_blocks=3, name="synthetic") -> Workload:
+    """A small seeded problem with discriminating options for parity tests.
+
+    Sequence s has k_lens[s] tokens of which the last q_lens[s] are new.  With
+    ``paged`` the earlier k_lens[s] - q_lens[s] tokens form a ``prefix`` phase
+    (cached history, stored first) and attention reads the pools; without it
+    q_lens must equal k_lens and attention reads the flat k/v.
+    Options: ``q_scale`` multiplies q (8 gives a peaky softmax), ``q_zero``
+    makes every weight equal, ``v_position`` writes each value row's position
+    into its first two elements as (j mod 16)/16 and ((j div 16) mod 16)/16.
+    """
+    meta, _, r_pre, r_fix, _ = _streams(seed)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    k_lens = np.asarray(k_lens, dtype=np.int64)
+    if (q_lens > k_lens).any() or (not paged and (q_lens != k_lens).any()):
+        raise ValueError("need q_len <= k_len, and equal lengths without a cache")
+    S = len(q_lens)
+    Hq, Hkv, d, bs = num_q_heads, num_kv_heads, head_dim, block_size
+    nb = [max(_blocks_for(n, bs), 1) for n in k_lens]
+    NB = int(sum(nb)) + extra_blocks
+    perm = meta.permutation(NB).astype(np.int32)
+    bt = _tables(perm, nb, max(nb))
+    prefill = _phase(r_pre, q_lens, k_lens, Hq, Hkv, d, paged=paged)
+    hist_lens = k_lens - q_lens
+    prefix = None
+    if paged and hist_lens.sum() > 0:
+        prefix = _phase(r_fix, hist_lens, hist_lens, Hq, Hkv, d, paged=True)
+    if q_zero:
+        prefill.q[:] = 0
+    elif q_scale != 1.0:
+        prefill.q[:] = f32_to_bf16_bits(bf16_bits_to_f32(prefill.q) * np.float32(q_scale))
+    if v_position:
+        for ph, first in ((prefix, np.zeros(S, np.int64)), (prefill, hist_lens)):
+            if ph is None:
+                continue
+            for s in range(S):
+                a, b = ph.cu_seqlens_q[s], ph.cu_seqlens_q[s + 1]
+                j = first[s] + np.arange(b - a)
+                ph.v[a:b, :, 0] = f32_to_bf16_bits(((j % 16) / 16.0).astype(np.float32))[:, None]
+                ph.v[a:b, :, 1] = f32_to_bf16_bits((((j // 16) % 16) / 16.0).astype(np.float32))[:, None]
+    wl = Workload(name, "synthetic parity problem", Hq, Hkv, d, bs, NB, _scale(d), bt,
+                  _nan_pool(NB, bs, Hkv, d), _nan_pool(NB, bs, Hkv, d), prefix=prefix,
+                  prefill=prefill)
+    wl.extra["prefix_per_seq"] = True
+    return wl

@@ -1,0 +1,84 @@
+"""Decode step (store new K/V -> split-K -> reduce) captured once in a HIP graph
+and replayed with new values and new context lengths inside the captured
+maxima ("nano-vLLM offline" course, item 03: replay reads new inputs and
+computes new results; "Visual atlas" ch.26: preallocated buffers, values and
+valid lengths may change, the shape/address contract must hold).
+
+Every replay is checked against a fresh oracle run on the same inputs, with
+eager library calls and synchronisations between replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+from pipelines import check_close, dev_bf16, dev_i32, host_f64, host_u16, log, prefix_tables
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_graph_replays(orc):
+    import paged_kv_attention_27_amd as pa
+    from paged_kv_attention_27_amd import workloads
+    S, Hq, Hkv, d, bs = 6, 16, 8, 128, 256
+    cap = [300, 1024, 2048, 700, 4096, 512]          # tokens each sequence may reach
+    wl = workloads.synthetic(q_lens=[1] * S, k_lens=cap, block_size=bs, seed=31)
+    # history: every position below cap-1 is stored once up front
+    kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
+    ok, ov = wl.k_cache.copy(), wl.v_cache.copy()
+    ph = wl.prefix
+    pa.pa_store_kv(dev_bf16(ph.k), dev_bf16(ph.v), kc, vc,
+                   pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, prefix_tables(wl), bs).cuda())
+    orc.store(ph.k, ph.v, orc.slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, prefix_tables(wl), bs),
+              ok, ov)
+
+    max_ctx = max(cap)
+    bt = dev_i32(wl.block_tables)
+    q_s = torch.empty((S, Hq, d), dtype=torch.bfloat16, device="cuda")
+    k_s = torch.empty((S, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    v_s = torch.empty((S, Hkv, d), dtype=torch.bfloat16, device="cuda")
+    slots_s = torch.empty(S, dtype=torch.int32, device="cuda")
+    ctx_s = torch.ones(S, dtype=torch.int32, device="cuda")
+    out_s = torch.empty((S, Hq, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(pa.pa_decode_workspace_size(S, Hq, Hkv, d, max_ctx), dtype=torch.uint8,
+                     device="cuda")
+    slots_s.fill_(-1)   # capture-time run stores nothing
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            pa.pa_store_kv(k_s, v_s, kc, vc, slots_s, stream=stream)
+            pa.pa_decode(q_s, kc, vc, bt, ctx_s, max_ctx, wl.scale, workspace=ws, out=out_s,
+                         stream=stream)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(77)
+    for r in range(4):
+        ctx = np.array([rng.integers(1, c + 1) for c in cap], np.int32)
+        if r == 3:
+            ctx = np.array(cap, np.int32)
+        q = workloads.normal_bf16(rng, (S, Hq, d), 2.0)
+        k = workloads.normal_bf16(rng, (S, Hkv, d))
+        v = workloads.normal_bf16(rng, (S, Hkv, d))
+        cu1 = np.arange(S + 1, dtype=np.int32)
+        slots = pa.pa_slot_mapping(cu1, ctx, wl.block_tables, bs)
+        q_s.copy_(dev_bf16(q))
+        k_s.copy_(dev_bf16(k))
+        v_s.copy_(dev_bf16(v))
+        slots_s.copy_(slots.cuda())
+        ctx_s.copy_(dev_i32(ctx))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host_f64(out_s)
+        # eager work between replays: a plain call on the default stream
+        eager = pa.pa_decode(dev_bf16(q), kc, vc, bt, dev_i32(ctx), max_ctx, wl.scale)
+        torch.cuda.synchronize()
+
+        orc.store(k, v, orc.slot_mapping(cu1, ctx, wl.block_tables, bs), ok, ov)
+        ref = orc.decode(q, ok, ov, wl.block_tables, ctx, wl.scale)
+        log(f"replay {r}: ctx={ctx.tolist()}")
+        check_close(got, ref, f"graph replay {r}")
+        assert np.array_equal(host_u16(out_s), host_u16(eager)), "replay differs from eager call"
+    assert np.array_equal(host_u16(kc), ok) and np.array_equal(host_u16(vc), ov)
