@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Workload of the headline line: batched paged decode, 256 sequences with
+context lengths U[128, 4096] (new token included), Hq=16 / Hkv=8 / d=128,
+block size 256, 4096-block pool, seeded N(0,1) inputs.  One step is one decode
+round: store the 256 new K/V rows, split-K attention, reduce; the three
+launches are captured once in a HIP graph and replayed, as a serving loop
+would.  ``value`` = algorithmic KV bytes of one step (each K/V element of
+every sequence's history read once) / measured step time, in GB/s.
+
+The same run also measures, as sub-objects of the JSON line:
+  * ``prefill``: the varlen prefill round (store + attention) on the 8-sequence
+    no-cache batch and on the 16-sequence prefix-cache batch, in TFLOP/s of
+    algorithmic work (two GEMMs over visible query/key pairs only);
+  * ``decode_long``: the 16 x 32768-token decode (Hq=32, group of 4).
+``roofline`` is the dominant kernel of the headline step (the split-K decode
+pass), timed alone with HIP events on its own stream; ``cpu_baseline`` is
+the fp64 CPU oracle timed on a bounded sample of the same decode workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "paged decode KV GB/s (% HBM peak); varlen prefill TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DECODE_SRC = os.path.join(ROOT, "paged_kv_attention_27_amd", "csrc", "decode.hip")
+PREFILL_SRC = os.path.join(ROOT, "paged_kv_attention_27_amd", "csrc", "prefill.hip")
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key, src, launches_bytes_unit=1.0):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != sha(src):
+        return None
+    return t["bytes_per_launch"]
+
+
+def dev_bf16(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def dev_i32(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def decode_kv_bytes(wl, ctx):
+    return int(np.sum(ctx.astype(np.int64))) * wl.num_kv_heads * wl.head_dim * 2 * 2
+
+
+def prefill_flops(wl, ph):
+    q = np.diff(ph.cu_seqlens_q).astype(np.int64)
+    k = ph.seqlens_k.astype(np.int64)
+    pairs = np.sum(q * (k - q) + q * (q + 1) // 2)
+    return int(4 * wl.num_q_heads * wl.head_dim * pairs)
+
+
+class DecodeSetup:
+    """Device state of one decode workload, plus its captured step graph."""
+
+    def __init__(self, torch, pa, wl, partition_size):
+        self.torch, self.pa, self.wl = torch, pa, wl
+        ph = wl.decode
+        self.kc = dev_bf16(torch, wl.k_cache)
+        self.vc = dev_bf16(torch, wl.v_cache)
+        self.bt = dev_i32(torch, wl.block_tables)
+        self.ctx = dev_i32(torch, ph.seqlens_k)
+        self.q = dev_bf16(torch, ph.q)
+        self.k = dev_bf16(torch, ph.k)
+        self.v = dev_bf16(torch, ph.v)
+        self.max_ctx = int(ph.seqlens_k.max())
+        self.part = partition_size
+        slots = pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, wl.block_size)
+        self.slots = slots.cuda()
+        S, Hq, d = ph.q.shape
+        self.out = torch.empty((S, Hq, d), dtype=torch.bfloat16, device="cuda")
+        need = pa.pa_decode_workspace_size(S, Hq, wl.num_kv_heads, d, self.max_ctx, partition_size)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        self.stream = torch.cuda.Stream()
+        self.bytes = decode_kv_bytes(wl, ph.seqlens_k)
+        self.n_part = pa.pa_decode_num_partitions(S, wl.num_kv_heads, self.max_ctx, partition_size)
+        torch.cuda.synchronize()
+
+    def args(self):
+        return (self.q, self.kc, self.vc, self.bt, self.ctx, self.max_ctx, self.wl.scale, self.ws,
+                self.out, self.part, self.stream)
+
+    def step_eager(self):
+        self.pa.pa_store_kv(self.k, self.v, self.kc, self.vc, self.slots, stream=self.stream)
+        self.pa.pa_decode(*self.args())
+
+    def capture(self):
+        torch = self.torch
+        self.step_eager()                    # warm the launch path outside capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(self.graph, stream=self.stream):
+                self.step_eager()
+        torch.cuda.synchronize()
+
+    def time_steps(self, steps, warmup):
+        torch = self.torch
+        for _ in range(warmup):
+            self.graph.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(self.stream)
+        for _ in range(steps):
+            with torch.cuda.stream(self.stream):
+                self.graph.replay()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / steps, wall
+
+    def time_kernels(self, iters):
+        """Average duration of the store, split-K and reduce launches (HIP events
+        recorded on the stream the kernels run on)."""
+        torch, pa = self.torch, self.pa
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+        for i in range(iters):
+            e = ev[i]
+            e[0].record(self.stream)
+            pa.pa_store_kv(self.k, self.v, self.kc, self.vc, self.slots, stream=self.stream)
+            e[1].record(self.stream)
+            pa.pa_decode_split(*self.args())
+            e[2].record(self.stream)
+            pa.pa_decode_reduce(*self.args())
+            e[3].record(self.stream)
+        torch.cuda.synchronize()
+        ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
+        return ms.mean(axis=0)   # store, split, reduce
+
+
+class PrefillSetup:
+    def __init__(self, torch, pa, wl):
+        self.torch, self.pa, self.wl = torch, pa, wl
+        ph = wl.prefill
+        self.kc = dev_bf16(torch, wl.k_cache)
+        self.vc = dev_bf16(torch, wl.v_cache)
+        self.bt = dev_i32(torch, wl.block_tables)
+        self.stream = torch.cuda.Stream()
+        if wl.prefix is not None:   # the cached prefix is stored once, before timing
+            fx = wl.prefix
+            s = wl.extra.get("prefix_seq", None)
+            tables = wl.block_tables if s is None else np.ascontiguousarray(wl.block_tables[s:s + 1])
+            slots = pa.pa_slot_mapping(fx.cu_seqlens_q, fx.seqlens_k, tables, wl.block_size)
+            pa.pa_store_kv(dev_bf16(torch, fx.k), dev_bf16(torch, fx.v), self.kc, self.vc,
+                           slots.cuda())
+        self.q = dev_bf16(torch, ph.q)
+        self.k = dev_bf16(torch, ph.k)
+        self.v = dev_bf16(torch, ph.v)
+        self.slots = pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables,
+                                        wl.block_size).cuda()
+        self.cu_q = dev_i32(torch, ph.cu_seqlens_q)
+        cu_k = ph.cu_seqlens_k if not ph.paged else np.concatenate(
+            [[0], np.cumsum(ph.seqlens_k)]).astype(np.int32)
+        self.cu_k = dev_i32(torch, cu_k)
+        self.out = torch.empty_like(self.q)
+        self.flops = prefill_flops(wl, ph)
+        torch.cuda.synchronize()
+
+    def attention(self):
+        wl, ph, pa = self.wl, self.wl.prefill, self.pa
+        if ph.paged:
+            pa.pa_prefill_varlen(self.q, None, None, self.kc, self.vc, self.bt, self.cu_q, self.cu_k,
+                                 ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale,
+                                 out=self.out, stream=self.stream)
+        else:
+            pa.pa_prefill_varlen(self.q, self.k, self.v, None, None, None, self.cu_q, self.cu_k,
+                                 ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale,
+                                 out=self.out, stream=self.stream)
+
+    def time(self, steps, warmup):
+        torch, pa = self.torch, self.pa
+        for _ in range(warmup):
+            pa.pa_store_kv(self.k, self.v, self.kc, self.vc, self.slots, stream=self.stream)
+            self.attention()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(self.stream)
+            pa.pa_store_kv(self.k, self.v, self.kc, self.vc, self.slots, stream=self.stream)
+            ev[i][1].record(self.stream)
+            self.attention()
+            ev[i][2].record(self.stream)
+        torch.cuda.synchronize()
+        ms = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev])
+        return ms.mean(axis=0)   # store, attention
+
+
+def cpu_baseline(wl, budget_s):
+    """The fp64 oracle on a bounded sample of the decode workload (first n
+    sequences, new tokens stored first), in KV GB/s."""
+    import oracle
+    orc = oracle.get()
+    ph = wl.decode
+    kc, vc = wl.k_cache, wl.v_cache      # host copies; the GPU holds its own
+    slots = orc.slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, wl.block_size)
+    orc.store(ph.k, ph.v, slots, kc, vc)
+
+    def run(n):
+        t0 = time.perf_counter()
+        orc.decode(np.ascontiguousarray(ph.q[:n]), kc, vc,
+                   np.ascontiguousarray(wl.block_tables[:n]),
+                   np.ascontiguousarray(ph.seqlens_k[:n]), wl.scale)
+        return time.perf_counter() - t0
+
+    S = wl.num_seqs
+    n = min(16, S)
+    t = run(n)
+    rate = decode_kv_bytes(wl, ph.seqlens_k[:n]) / max(t, 1e-6)
+    total = decode_kv_bytes(wl, ph.seqlens_k)
+    if total / rate > budget_s:
+        # largest prefix of sequences that fits the budget
+        cum = np.cumsum(ph.seqlens_k.astype(np.int64)) * wl.num_kv_heads * wl.head_dim * 4
+        n = int(max(1, np.searchsorted(cum, rate * budget_s)))
+    else:
+        n = S
+    t = run(n)
+    b = decode_kv_bytes(wl, ph.seqlens_k[:n])
+    return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 decode of the first {n} of {S} sequences ({b / 1e9:.3f} GB of KV, "
+                      f"new tokens stored first), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--partition", type=int, default=0, help="decode partition size (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill and long-decode sub-measurements")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_attention_27_amd as pa
+    from paged_kv_attention_27_amd import workloads
+    pa.load()
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device {dev.name} ({dev.gcnArchName if hasattr(dev, 'gcnArchName') else ''})")
+
+    log("generating the 256-sequence decode workload")
+    wl = workloads.make(4)
+    dset = DecodeSetup(torch, pa, wl, args.partition)
+    dset.capture()
+    log(f"timing {args.steps} graph-replayed decode steps")
+    ms_step, wall = dset.time_steps(args.steps, args.warmup)
+    k_store, k_split, k_reduce = dset.time_kernels(max(args.steps, 10))
+    value = dset.bytes / (ms_step * 1e-3) / 1e9
+    achieved = dset.bytes / (k_split * 1e-3) / 1e9
+    split_traffic = traffic_for("decode_split_c4", DECODE_SRC)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "batched paged decode: 256 seqs, ctx U[128,4096] incl. new token, "
+                               "Hq16/Hkv8/d128, block 256, 4096-block pool; step = store new "
+                               "K/V + split-K + reduce (HIP graph)",
+                   "num_seqs": wl.num_seqs, "sum_context": int(wl.decode.seqlens_k.sum()),
+                   "kv_bytes_per_step": dset.bytes, "partition_tokens":
+                       args.partition or "auto", "num_partitions": dset.n_part,
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"kernel": "decode_split_kernel (split-K pass)", "bound": "hbm",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": split_traffic,
+                     "launch_ms": {"store": round(float(k_store), 5), "split": round(float(k_split), 5),
+                                   "reduce": round(float(k_reduce), 5)}},
+    }
+    log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s; split {k_split * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s), reduce {k_reduce * 1e3:.1f} us, store {k_store * 1e3:.1f} us")
+    del dset
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        prefill = {}
+        for cfg in (2, 3):
+            pwl = workloads.make(cfg)
+            ps = PrefillSetup(torch, pa, pwl)
+            t_store, t_attn = ps.time(max(args.steps, 10), args.warmup)
+            tflops = ps.flops / (t_attn * 1e-3) / 1e12
+            prefill[pwl.name] = {
+                "value": round(tflops, 2), "unit": "TFLOP/s", "flops": ps.flops,
+                "ms_attention": round(float(t_attn), 5), "ms_store": round(float(t_store), 5),
+                "roofline": {"kernel": "prefill_kernel", "bound": "mfma",
+                             "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": traffic_for(f"prefill_{pwl.name}", PREFILL_SRC)}}
+            log(f"prefill {pwl.name}: attention {t_attn * 1e3:.1f} us = {tflops:.1f} TFLOP/s, "
+                f"store {t_store * 1e3:.1f} us")
+            del ps
+        result["prefill"] = prefill
+        lwl = workloads.make(5)
+        ls = DecodeSetup(torch, pa, lwl, args.partition)
+        ls.capture()
+        l_ms, _ = ls.time_steps(max(args.steps // 2, 5), args.warmup)
+        _, l_split, l_reduce = ls.time_kernels(max(args.steps // 2, 5))
+        result["decode_long"] = {
+            "workload": "16 seqs x 32768 ctx, Hq32/Hkv8/d128, block 256, 2048-block pool",
+            "value": round(ls.bytes / (l_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "ms_per_step": round(l_ms, 5), "num_partitions": ls.n_part,
+            "split_GBs": round(ls.bytes / (l_split * 1e-3) / 1e9, 2),
+            "ms_split": round(float(l_split), 5), "ms_reduce": round(float(l_reduce), 5)}
+        log(f"long decode: {l_ms * 1e3:.1f} us/step, split {l_split * 1e3:.1f} us")
+        del ls, lwl
+        torch.cuda.empty_cache()
+
+    if args.calibrate_copy:
+        n = 1 << 29   # bf16 elements: 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration"] = {"bytes_read": 2 * n, "bytes_written": 2 * n, "launches": 3}
+        del src, dst
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
