@@ -8,11 +8,15 @@
 //     KV head, sequence).  The g = Hq/Hkv query heads of the group share every
 //     K/V row the workgroup loads (GQA without a physical repeat, "Visual
 //     atlas" ch.18).  A token's 256-byte K row is read by 16 lanes x 16 bytes,
-//     so each wave64 load instruction moves four whole rows; every wave keeps
-//     U rows of K and of V per lane group in flight at once.  Dot products use
-//     v_dot2_f32_bf16 and a 4-step DPP row reduction; the softmax runs online
-//     in the log2 domain (scale * log2 e folded into the scores).  Each wave
-//     keeps its own running max/sum/output; the four waves are merged in LDS.
+//     so each wave64 load instruction moves four whole rows; a wave iteration
+//     covers 4*U keys and keeps 2*U loads per lane in flight.  When the block
+//     size is a multiple of 4*U the iteration's keys share one block, found by
+//     one scalar table lookup.  Scores use v_dot2_f32_bf16 and a 4-step DPP row
+//     reduction; weighted values use v_dot2_f32_bf16 over pairs of keys, with
+//     the weights rounded to bf16 (the same rounding the prefill MFMA applies).
+//     The softmax runs online in the log2 domain with a lazily updated running
+//     max (rescale only when it grows by more than 2^8).  Each wave keeps its
+//     own running max/sum/output; the four waves are merged in LDS.
 //   * If a sequence fits in one partition, that workgroup writes the final
 //     bf16 output; otherwise it writes the partition's running max, sum and
 //     unnormalised output row (fp32) to the workspace and
@@ -29,13 +33,9 @@ namespace {
 constexpr int D = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kTableCache = 1024;
+constexpr float kLazyTau = 8.0f;   // log2 growth of a running max tolerated before rescaling
 
-__device__ __forceinline__ int block_of(int j, int bs, int shift) {
-    return shift >= 0 ? (j >> shift) : (j / bs);
-}
-
-template <int G, int U>
+template <int G, int U, bool CHUNK_IN_BLOCK>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 {
     const int p = blockIdx.x;
@@ -55,19 +55,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     const int r = lane >> 4;   // lane group: which of the four rows a load instruction covers
     const int c = lane & 15;   // 8-element slice of the head dimension
 
-    __shared__ int32_t tbl[kTableCache];
     __shared__ float red_m[kWaves][G];
     __shared__ float red_l[kWaves][G];
     __shared__ float red_o[kWaves][G][D];
 
     const int bs = a.block_size, shift = a.bs_shift;
-    const int blk_first = block_of(t_begin, bs, shift);
-    const int blk_last = block_of(t_end - 1, bs, shift);
     const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
-    for (int i = tid; i <= blk_last - blk_first; i += kThreads)
-        tbl[i] = bt_row[blk_first + i];
-
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    const int64_t row_elems = (int64_t)Hkv * D;
+
     const bf16 *q = static_cast<const bf16 *>(a.q);
     uint32_t qw[G][4];
 #pragma unroll
@@ -75,7 +71,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
         const uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)s * Hq + kvh * G + h) * D + 8 * c);
         qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
     }
-    __syncthreads();
 
     float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -89,27 +84,44 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     const bf16 *kc = static_cast<const bf16 *>(a.k_cache);
     const bf16 *vc = static_cast<const bf16 *>(a.v_cache);
     const float sl2 = a.scale_log2;
-    constexpr int kChunk = 4 * U;   // keys per wave iteration
+    const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    constexpr int kChunk = 4 * U;   // keys per wave iteration (lane group r owns U consecutive keys)
     const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
+    const int64_t lane_off = (int64_t)(r * U) * row_elems + kvh * D + 8 * c;
 
     for (int ch = wave; ch < n_chunks; ch += kWaves) {
-        const int base = t_begin + ch * kChunk + r * U;
+        const int cs = t_begin + ch * kChunk;
+        const int base = cs + r * U;
         uint4 kr[U], vr[U];
+        if (CHUNK_IN_BLOCK) {
+            // the whole chunk lies in one block: one (scalar) table lookup
+            const int lb = __builtin_amdgcn_readfirstlane(shift >= 0 ? (cs >> shift) : (cs / bs));
+            const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(bt_row[lb]) * bs + (cs - lb * bs);
+            const bf16 *kb = kc + row0 * row_elems + lane_off;
+            const bf16 *vb = vc + row0 * row_elems + lane_off;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = base + u;
-            if (j < t_end) {
-                const int lb = block_of(j, bs, shift);
-                const int64_t row = (int64_t)tbl[lb - blk_first] * bs + (j - lb * bs);
-                const int64_t off = (row * Hkv + kvh) * D + 8 * c;
-                kr[u] = *reinterpret_cast<const uint4 *>(kc + off);
-                vr[u] = *reinterpret_cast<const uint4 *>(vc + off);
-            } else {
-                kr[u] = make_uint4(0, 0, 0, 0);
-                vr[u] = make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < U; ++u) {
+                const bool ok = base + u < t_end;
+                kr[u] = ok ? *reinterpret_cast<const uint4 *>(kb + u * row_elems) : make_uint4(0, 0, 0, 0);
+                vr[u] = ok ? *reinterpret_cast<const uint4 *>(vb + u * row_elems) : make_uint4(0, 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int j = base + u;
+                if (j < t_end) {
+                    const int lb = shift >= 0 ? (j >> shift) : (j / bs);
+                    const int64_t off = ((int64_t)bt_row[lb] * bs + (j - lb * bs)) * row_elems + kvh * D + 8 * c;
+                    kr[u] = *reinterpret_cast<const uint4 *>(kc + off);
+                    vr[u] = *reinterpret_cast<const uint4 *>(vc + off);
+                } else {
+                    kr[u] = make_uint4(0, 0, 0, 0);
+                    vr[u] = make_uint4(0, 0, 0, 0);
+                }
             }
         }
 
+        // raw scores q.k (all 16 lanes of a group hold the bit-identical total)
         float sc[G][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -125,11 +137,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
                                                      __builtin_bit_cast(bf16x2, kr[u].z), d0, false);
                 d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][3]),
                                                      __builtin_bit_cast(bf16x2, kr[u].w), d0, false);
-                const float dot = row16_sum(d0);
-                sc[h][u] = valid ? dot * sl2 : -INFINITY;
+                sc[h][u] = valid ? row16_sum(d0) : -INFINITY;
             }
         }
 
+        // lazy running max: rescale only when some head's max grew by more than 2^8
+        bool grow_any = false;
+        float mcand[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             float mx = sc[h][0];
@@ -137,27 +151,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
             for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[h][u]);
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            const float mnew = fmaxf(m[h], mx);
-            const float alpha = fast_exp2(m[h] - mnew);
-            m[h] = mnew;
-            l[h] *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+            mcand[h] = mx * sl2;
+            grow_any |= mcand[h] > m[h] + kLazyTau;
         }
-
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[8];
-            vf[0] = bf16_lo(vr[u].x); vf[1] = bf16_hi(vr[u].x);
-            vf[2] = bf16_lo(vr[u].y); vf[3] = bf16_hi(vr[u].y);
-            vf[4] = bf16_lo(vr[u].z); vf[5] = bf16_hi(vr[u].z);
-            vf[6] = bf16_lo(vr[u].w); vf[7] = bf16_hi(vr[u].w);
+        if (grow_any) {   // wave-uniform: the maxima are reduced over the whole wave
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float pw = fast_exp2(sc[h][u] - m[h]);
-                l[h] += pw;
+                const float mnew = fmaxf(m[h], mcand[h]);
+                const float alpha = fast_exp2(m[h] - mnew);
+                m[h] = mnew;
+                l[h] *= alpha;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pw, vf[e], acc[h][e]);
+                for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+            }
+        }
+
+        // weighted values, two keys at a time: v_dot2 over (p_u, p_u+1) x (v_u, v_u+1)
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+            uint32_t vlo[4], vhi[4];
+            const uint32_t w0[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+            const uint32_t w1[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                vlo[w] = __builtin_amdgcn_perm(w1[w], w0[w], 0x05040100u);   // (v_u[2w],   v_u+1[2w])
+                vhi[w] = __builtin_amdgcn_perm(w1[w], w0[w], 0x07060302u);   // (v_u[2w+1], v_u+1[2w+1])
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float p0 = fast_exp2(fmaf(sc[h][u], sl2, -m[h]));
+                const float p1 = fast_exp2(fmaf(sc[h][u + 1], sl2, -m[h]));
+                const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                l[h] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l[h], false);
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    acc[h][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vlo[w]),
+                                                                    acc[h][2 * w], false);
+                    acc[h][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vhi[w]),
+                                                                        acc[h][2 * w + 1], false);
+                }
             }
         }
     }
@@ -246,7 +278,10 @@ hipError_t launch_g(const DecodeArgs &a, int passes, hipStream_t stream)
 {
     if (passes & 1) {
         dim3 grid(a.n_part, a.num_kv_heads, a.num_seqs);
-        hipLaunchKernelGGL((decode_split_kernel<G, U>), grid, dim3(kThreads), 0, stream, a);
+        if (a.block_size % (4 * U) == 0)
+            hipLaunchKernelGGL((decode_split_kernel<G, U, true>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((decode_split_kernel<G, U, false>), grid, dim3(kThreads), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;

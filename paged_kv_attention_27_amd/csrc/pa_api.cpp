@@ -11,8 +11,7 @@
 namespace {
 
 constexpr int kHeadDim = 128;
-constexpr int32_t kDefaultPartition = 512;
-constexpr int kDecodeTableCache = 1024;   // table entries one decode workgroup caches
+constexpr int64_t kDecodeTargetWorkgroups = 4096;   // ~16 per CU on 256 CUs
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -31,8 +30,19 @@ bool group_supported(int32_t hq, int32_t hkv) {
     return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
-int32_t resolve_partition(int32_t partition_size) {
-    return partition_size == 0 ? kDefaultPartition : partition_size;
+// Library's decode partition size: the smallest power of two >= 256 that
+// keeps the (partition, KV head, sequence) grid near 4096 workgroups, at most
+// 8192 keys.  Fewer, longer partitions cut per-workgroup start-up and the
+// partials' traffic; enough of them keep every CU busy.  Host integers only.
+int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
+                          int32_t max_context_len) {
+    if (partition_size != 0)
+        return partition_size;
+    const int64_t work = (int64_t)num_seqs * num_kv_heads * max_context_len;
+    int32_t part = 256;
+    while (part < 8192 && (int64_t)part * kDecodeTargetWorkgroups < work)
+        part *= 2;
+    return part;
 }
 
 int32_t num_partitions(int32_t max_context_len, int32_t part) {
@@ -172,7 +182,8 @@ int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t
     if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0 || partition_size < 0 ||
         partition_size % 32 != 0)
         return 0;
-    return num_partitions(max_context_len, resolve_partition(partition_size));
+    return num_partitions(max_context_len, resolve_partition(partition_size, num_seqs,
+                                                             num_kv_heads, max_context_len));
 }
 
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -210,9 +221,8 @@ int decode_passes(const void *q, const void *k_cache, const void *v_cache,
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0)
         return PA_OK;
-    const int32_t part = resolve_partition(partition_size);
-    if ((part - 1) / block_size + 2 > kDecodeTableCache)
-        return PA_ERR_UNSUPPORTED;
+    const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads,
+                                           max_context_len);
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
         return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))

@@ -113,7 +113,6 @@ def test_decode_validation(lib):
     assert _decode(lib, hq=24, hkv=8) == UNSUPPORTED
     assert _decode(lib, scale=-1.0) == SHAPE
     assert _decode(lib, q=None) == NULL
-    assert _decode(lib, bs=1, maxb=8192, mctx=8192, part=2048) == UNSUPPORTED  # table cache
     assert _decode(lib, S=0, q=None) == OK
 
 
@@ -125,7 +124,11 @@ def test_decode_sizes(lib):
     assert np_(4, 8, 0, 512) == 1
     assert np_(4, 8, 100, 33) == 0
     assert lib.pa_decode_workspace_size(3, 16, 8, 128, 1000, 256) == 3 * 16 * 4 * 130 * 4
-    assert np_(4, 8, 5000, 0) >= 1
+    assert np_(256, 8, 4096, 0) == 2      # auto: 2048-key partitions
+    assert np_(16, 8, 32768, 0) == 32     # auto: 1024-key partitions
+    assert np_(4, 8, 512, 0) == 2         # auto: at least 256 keys
+    assert np_(64, 8, 10**6, 0) == 123    # auto: at most 8192 keys
+    assert np_(1, 1, 10**6, 0) == 3907    # auto: 256 keys keep one sequence busy
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
