@@ -10,8 +10,8 @@
 //     atlas" ch.18).  A token's 256-byte K row is read by 16 lanes x 16 bytes,
 //     so each wave64 load instruction moves four whole rows; a wave iteration
 //     covers 4*U keys and keeps 2*U loads per lane in flight.  When the block
-//     size is a multiple of 4*U the iteration's keys share one block, found by
-//     one scalar table lookup.  Scores use v_dot2_f32_bf16 and a 4-step DPP row
+//     and partition sizes are multiples of 4*U the iteration's keys share one
+//     block, found by one scalar table lookup.  Scores use v_dot2_f32_bf16 and a 4-step DPP row
 //     reduction; weighted values use v_dot2_f32_bf16 over pairs of keys, with
 //     the weights rounded to bf16 (the same rounding the prefill MFMA applies).
 //     The softmax runs online in the log2 domain with a lazily updated running
@@ -246,31 +246,62 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     }
 }
 
-__global__ __launch_bounds__(D) void decode_reduce_kernel(DecodeArgs a)
+constexpr int kReduceThreads = 256;   // two Q heads of one sequence per workgroup
+constexpr int kReduceStage = 512;     // partitions staged in LDS per pass
+
+__global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArgs a)
 {
-    const int h = blockIdx.x;
+    const int hh = threadIdx.x / D;          // which of the workgroup's two heads
+    const int dd = threadIdx.x % D;
+    const bool active = 2 * (int)blockIdx.x + hh < a.num_q_heads;   // odd Hq: last half idles
+    const int h = active ? 2 * blockIdx.x + hh : a.num_q_heads - 1;
     const int s = blockIdx.y;
-    const int dd = threadIdx.x;
     const int ctx = a.context_lens[s];
-    const int np = (ctx + a.part_tokens - 1) / a.part_tokens;
+    const int np = (ctx + a.part_tokens - 1) / a.part_tokens;   // uniform over the workgroup
     if (np == 1)
-        return;  // the single partition wrote the output itself
+        return;  // a single partition wrote the output itself
     uint16_t *out = static_cast<uint16_t *>(a.out) + ((int64_t)s * a.num_q_heads + h) * D + dd;
     if (np <= 0) {
-        *out = 0;  // empty context: defined as a zero row
+        if (active)
+            *out = 0;  // empty context: defined as a zero row
         return;
     }
     const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.n_part;
-    const float *ml = a.ws_ml + base * 2;
+    const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + base;
+    const float *wo = a.ws_o + base * D + dd;
+
+    // global max over the partitions: every thread of the head scans a slice, then LDS
+    __shared__ float red[2][D];
     float M = kMaxFloor;
-    for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.f, o = 0.f;
-    for (int p = 0; p < np; ++p) {
-        const float f = fast_exp2(ml[2 * p] - M);
-        L = fmaf(f, ml[2 * p + 1], L);
-        o = fmaf(f, a.ws_o[(base + p) * D + dd], o);
+    for (int p = dd; p < np; p += D) M = fmaxf(M, ml[p].x);
+    red[hh][dd] = M;
+    __syncthreads();
+    for (int w = D / 2; w > 0; w /= 2) {
+        if (dd < w) red[hh][dd] = fmaxf(red[hh][dd], red[hh][dd + w]);
+        __syncthreads();
     }
-    *out = f32_to_bf16_bits(o / L);
+    M = red[hh][0];
+
+    // weights 2^(m_p - M) staged in LDS, then independent loads of the partial rows
+    __shared__ float2 wl[2][kReduceStage];
+    float L = 0.f, o = 0.f;
+    for (int p0 = 0; p0 < np; p0 += kReduceStage) {
+        const int n = min(kReduceStage, np - p0);
+        __syncthreads();
+        for (int i = dd; i < n; i += D) {
+            const float2 v = ml[p0 + i];
+            wl[hh][i] = make_float2(fast_exp2(v.x - M), v.y);
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int i = 0; i < n; ++i) {
+            const float2 w = wl[hh][i];
+            L = fmaf(w.x, w.y, L);
+            o = fmaf(w.x, wo[(int64_t)(p0 + i) * D], o);
+        }
+    }
+    if (active)
+        *out = f32_to_bf16_bits(o / L);
 }
 
 template <int G, int U>
@@ -278,7 +309,8 @@ hipError_t launch_g(const DecodeArgs &a, int passes, hipStream_t stream)
 {
     if (passes & 1) {
         dim3 grid(a.n_part, a.num_kv_heads, a.num_seqs);
-        if (a.block_size % (4 * U) == 0)
+        // one table lookup per iteration needs every 4U-key chunk inside one block
+        if (a.block_size % (4 * U) == 0 && a.part_tokens % (4 * U) == 0)
             hipLaunchKernelGGL((decode_split_kernel<G, U, true>), grid, dim3(kThreads), 0, stream, a);
         else
             hipLaunchKernelGGL((decode_split_kernel<G, U, false>), grid, dim3(kThreads), 0, stream, a);
@@ -287,8 +319,8 @@ hipError_t launch_g(const DecodeArgs &a, int passes, hipStream_t stream)
             return e;
     }
     if (passes & 2) {
-        hipLaunchKernelGGL(decode_reduce_kernel, dim3(a.num_q_heads, a.num_seqs), dim3(D), 0,
-                           stream, a);
+        hipLaunchKernelGGL(decode_reduce_kernel, dim3((a.num_q_heads + 1) / 2, a.num_seqs),
+                           dim3(kReduceThreads), 0, stream, a);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -299,8 +331,8 @@ hipError_t launch_g(const DecodeArgs &a, int passes, hipStream_t stream)
 hipError_t launch_decode(const DecodeArgs &a, int passes, hipStream_t stream)
 {
     switch (a.num_q_heads / a.num_kv_heads) {
-    case 1: return launch_g<1, 8>(a, passes, stream);
-    case 2: return launch_g<2, 8>(a, passes, stream);
+    case 1: return launch_g<1, 16>(a, passes, stream);
+    case 2: return launch_g<2, 16>(a, passes, stream);
     case 4: return launch_g<4, 8>(a, passes, stream);
     case 8: return launch_g<8, 4>(a, passes, stream);
     default: return hipErrorInvalidValue;

@@ -12,6 +12,7 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int64_t kDecodeTargetWorkgroups = 4096;   // ~16 per CU on 256 CUs
+constexpr int64_t kDecodeWholeSequencePairs = 2048;  // (sequence, KV head) pairs that fill the chip
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -30,19 +31,24 @@ bool group_supported(int32_t hq, int32_t hkv) {
     return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
-// Library's decode partition size: the smallest power of two >= 256 that
-// keeps the (partition, KV head, sequence) grid near 4096 workgroups, at most
-// 8192 keys.  Fewer, longer partitions cut per-workgroup start-up and the
-// partials' traffic; enough of them keep every CU busy.  Host integers only.
+// Library's decode partition size (host integers only).  With at least 2048
+// (sequence, KV head) pairs every sequence is one partition: the grid already
+// fills the chip, and whole-sequence workgroups need no partials or merge.
+// Otherwise the context is split so the grid holds about 4096 workgroups,
+// in multiples of 256 keys.
 int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
                           int32_t max_context_len) {
     if (partition_size != 0)
         return partition_size;
-    const int64_t work = (int64_t)num_seqs * num_kv_heads * max_context_len;
-    int32_t part = 256;
-    while (part < 8192 && (int64_t)part * kDecodeTargetWorkgroups < work)
-        part *= 2;
-    return part;
+    const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
+    int64_t n_part = 1;
+    if (pairs > 0 && pairs < kDecodeWholeSequencePairs)
+        n_part = (kDecodeTargetWorkgroups + pairs - 1) / pairs;
+    int64_t part = ((int64_t)max_context_len + n_part - 1) / n_part;
+    part = (part + 255) / 256 * 256;
+    if (part < 256)
+        part = 256;
+    return (int32_t)(part > (1 << 30) ? (1 << 30) : part);
 }
 
 int32_t num_partitions(int32_t max_context_len, int32_t part) {

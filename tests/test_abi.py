@@ -124,11 +124,11 @@ def test_decode_sizes(lib):
     assert np_(4, 8, 0, 512) == 1
     assert np_(4, 8, 100, 33) == 0
     assert lib.pa_decode_workspace_size(3, 16, 8, 128, 1000, 256) == 3 * 16 * 4 * 130 * 4
-    assert np_(256, 8, 4096, 0) == 2      # auto: 2048-key partitions
-    assert np_(16, 8, 32768, 0) == 32     # auto: 1024-key partitions
+    assert np_(256, 8, 4096, 0) == 1      # auto: 2048 pairs fill the chip, one partition
+    assert np_(16, 8, 32768, 0) == 32     # auto: 1024-key partitions, 4096 workgroups
     assert np_(4, 8, 512, 0) == 2         # auto: at least 256 keys
-    assert np_(64, 8, 10**6, 0) == 123    # auto: at most 8192 keys
-    assert np_(1, 1, 10**6, 0) == 3907    # auto: 256 keys keep one sequence busy
+    assert np_(1, 8, 10**6, 0) == 489     # auto: 1954 keys, rounded up to 2048
+    assert np_(1, 1, 1000, 0) == 4        # auto: rounded up to 256 keys
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
