@@ -6,10 +6,12 @@
 Workload of the headline line: batched paged decode, 256 sequences with
 context lengths U[128, 4096] (new token included), Hq=16 / Hkv=8 / d=128,
 block size 256, 4096-block pool, seeded N(0,1) inputs.  One step is one decode
-round: store the 256 new K/V rows, split-K attention, reduce; the three
-launches are captured once in a HIP graph and replayed, as a serving loop
-would.  ``value`` = algorithmic KV bytes of one step (each K/V element of
-every sequence's history read once) / measured step time, in GB/s.
+round: store the 256 new K/V rows and attend over every history
+(pa_decode_store: the store is fused into the attention kernel, plus the
+reduce pass when a context is split), captured once in a HIP graph and
+replayed, as a serving loop would.  ``value`` = algorithmic KV bytes of one
+step (each K/V element of every sequence's history read once) / measured step
+time, in GB/s.
 
 The same run also measures, as sub-objects of the JSON line:
   * ``prefill``: the varlen prefill round (store + attention) on the 8-sequence
@@ -17,8 +19,9 @@ The same run also measures, as sub-objects of the JSON line:
     algorithmic work (two GEMMs over visible query/key pairs only);
   * ``decode_long``: the 16 x 32768-token decode (Hq=32, group of 4).
 ``roofline`` is the dominant kernel of the headline step (the split-K decode
-pass), timed alone with HIP events on its own stream; ``cpu_baseline`` is
-the fp64 CPU oracle timed on a bounded sample of the same decode workload.
+pass with the fused store), timed alone with HIP events on its own stream;
+``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of the same
+decode workload.
 """
 from __future__ import annotations
 
@@ -113,8 +116,9 @@ class DecodeSetup:
                 self.out, self.part, self.stream)
 
     def step_eager(self):
-        self.pa.pa_store_kv(self.k, self.v, self.kc, self.vc, self.slots, stream=self.stream)
-        self.pa.pa_decode(*self.args())
+        self.pa.pa_decode_store(self.q, self.k, self.v, self.slots, self.kc, self.vc, self.bt,
+                                self.ctx, self.max_ctx, self.wl.scale, self.ws, self.out,
+                                self.part, self.stream)
 
     def capture(self):
         torch = self.torch
@@ -144,10 +148,11 @@ class DecodeSetup:
         return e0.elapsed_time(e1) / steps, wall
 
     def time_kernels(self, iters):
-        """Average duration of the store, split-K and reduce launches (HIP events
-        recorded on the stream the kernels run on)."""
+        """Average duration of each launch (HIP events recorded on the stream the
+        kernels run on): the unfused store, split-K and reduce passes, and the
+        fused store + split-K pass (followed by its reduce when partitioned)."""
         torch, pa = self.torch, self.pa
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(iters)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(iters)]
         for i in range(iters):
             e = ev[i]
             e[0].record(self.stream)
@@ -157,9 +162,11 @@ class DecodeSetup:
             e[2].record(self.stream)
             pa.pa_decode_reduce(*self.args())
             e[3].record(self.stream)
+            self.step_eager()
+            e[4].record(self.stream)
         torch.cuda.synchronize()
-        ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev])
-        return ms.mean(axis=0)   # store, split, reduce
+        ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+        return ms.mean(axis=0)   # store, split, reduce, fused step
 
 
 class PrefillSetup:
@@ -286,31 +293,37 @@ def main():
     dset.capture()
     log(f"timing {args.steps} graph-replayed decode steps")
     ms_step, wall = dset.time_steps(args.steps, args.warmup)
-    k_store, k_split, k_reduce = dset.time_kernels(max(args.steps, 10))
+    k_store, k_split, k_reduce, k_fused = dset.time_kernels(max(args.steps, 10))
     value = dset.bytes / (ms_step * 1e-3) / 1e9
-    achieved = dset.bytes / (k_split * 1e-3) / 1e9
-    split_traffic = traffic_for("decode_split_c4", DECODE_SRC)
+    # the fused step is a single kernel when every context fits one partition
+    k_roof = k_fused if dset.n_part == 1 else k_split
+    achieved = dset.bytes / (k_roof * 1e-3) / 1e9
+    split_traffic = traffic_for("decode_fused_c4", DECODE_SRC)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "batched paged decode: 256 seqs, ctx U[128,4096] incl. new token, "
-                               "Hq16/Hkv8/d128, block 256, 4096-block pool; step = store new "
-                               "K/V + split-K + reduce (HIP graph)",
+                               "Hq16/Hkv8/d128, block 256, 4096-block pool; step = fused store "
+                               "+ split-K attention (+ reduce when partitioned), HIP graph",
                    "num_seqs": wl.num_seqs, "sum_context": int(wl.decode.seqlens_k.sum()),
                    "kv_bytes_per_step": dset.bytes, "partition_tokens":
                        args.partition or "auto", "num_partitions": dset.n_part,
                    "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
-        "roofline": {"kernel": "decode_split_kernel (split-K pass)", "bound": "hbm",
+        "roofline": {"kernel": ("decode_split_kernel with fused store" if dset.n_part == 1
+                                else "decode_split_kernel (split-K pass)"), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": split_traffic,
-                     "launch_ms": {"store": round(float(k_store), 5), "split": round(float(k_split), 5),
-                                   "reduce": round(float(k_reduce), 5)}},
+                     "launch_ms": {"fused_step": round(float(k_fused), 5),
+                                   "unfused_store": round(float(k_store), 5),
+                                   "unfused_split": round(float(k_split), 5),
+                                   "unfused_reduce": round(float(k_reduce), 5)}},
     }
-    log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s; split {k_split * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s), reduce {k_reduce * 1e3:.1f} us, store {k_store * 1e3:.1f} us")
+    log(f"decode: {ms_step * 1e3:.1f} us/step, {value:.0f} GB/s; fused kernel {k_fused * 1e3:.1f} us "
+        f"({dset.bytes / (k_fused * 1e-3) / 1e9:.0f} GB/s); unfused store {k_store * 1e3:.1f} + "
+        f"split {k_split * 1e3:.1f} + reduce {k_reduce * 1e3:.1f} us")
     del dset
     torch.cuda.empty_cache()
 
@@ -336,7 +349,7 @@ def main():
         ls = DecodeSetup(torch, pa, lwl, args.partition)
         ls.capture()
         l_ms, _ = ls.time_steps(max(args.steps // 2, 5), args.warmup)
-        _, l_split, l_reduce = ls.time_kernels(max(args.steps // 2, 5))
+        _, l_split, l_reduce, _ = ls.time_kernels(max(args.steps // 2, 5))
         result["decode_long"] = {
             "workload": "16 seqs x 32768 ctx, Hq32/Hkv8/d128, block 256, 2048-block pool",
             "value": round(ls.bytes / (l_ms * 1e-3) / 1e9, 2), "unit": "GB/s",

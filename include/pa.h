@@ -170,8 +170,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * sum_j p_j v_j / sum_j p_j with p_j = exp(scale q.k_j - max).
  * The keys are split into partitions of partition_size tokens, each reduced
  * to a partial (running max, sum, unnormalised output) in the workspace, and
- * a second kernel combines the partials (log-sum-exp merge).  context_lens[s]
- * == 0 yields a zero output row.
+ * a second kernel combines the partials (log-sum-exp merge); with a single
+ * partition the first kernel writes the output and the second is not
+ * launched.  context_lens[s] == 0 yields a zero output row.
  *
  * q             (device) [num_seqs, num_q_heads, head_dim] bf16
  * k_cache/v_cache (device) pools as above
@@ -193,12 +194,39 @@ int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
 
 /*
+ * Fused decode step: the KV-cache store of each sequence's new token and the
+ * paged decode over its history, in one launch (plus the reduce pass when a
+ * context is split into several partitions).  Equivalent to
+ *     pa_store_kv(k_new, v_new, k_cache, v_cache, slot_mapping, num_seqs, ...)
+ *     pa_decode(q, k_cache, v_cache, ...)
+ * when slot_mapping[s] is the pool row of position context_lens[s] - 1 (as
+ * pa_slot_mapping computes it): the workgroup that owns that position writes
+ * the new K/V rows to the slot and attends to them from registers instead of
+ * re-reading the pool ([Atlas] ch.21: the sampled token has no K/V until its
+ * decode step; [Course] ACCURACY & SCOPE: the token's KV is written first).
+ * A negative slot skips the store and the position is read from the pool.
+ *
+ * k_new, v_new  (device) [num_seqs, num_kv_heads, head_dim] bf16, 16-byte aligned
+ * slot_mapping  (device) [num_seqs]
+ * context_lens  (device) [num_seqs], >= 1 for every sequence with a new token
+ * Other arguments as pa_decode; the outputs and pool contents equal the
+ * unfused pair's up to fp32 summation order.
+ */
+int pa_decode_store(const void *q, const void *k_new, const void *v_new,
+                    const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, int32_t partition_size, void *workspace,
+                    size_t workspace_bytes, void *out, hipStream_t stream);
+
+/*
  * The two passes of pa_decode, for callers that schedule or time them apart.
  * Arguments are those of pa_decode.  pa_decode_split runs the partition pass:
  * it writes the final output row of every sequence whose context fits in one
  * partition, and the partials of the others into the workspace.
- * pa_decode_reduce then merges the partials (and writes the zero rows of empty
- * contexts).  Calling pa_decode_split and then pa_decode_reduce on one stream
+ * pa_decode_reduce then merges the partials (nothing to do when every
+ * context fits one partition).  Calling pa_decode_split and then pa_decode_reduce on one stream
  * with the same arguments is exactly pa_decode.
  */
 int pa_decode_split(const void *q, const void *k_cache, const void *v_cache,

@@ -8,9 +8,10 @@ library is missing or returns an error.  See ``binding.py``.
 """
 from .binding import (PaError, library_path, load, pa_decode, pa_decode_workspace_size,  # noqa: F401
                       pa_prefill_varlen, pa_slot_mapping, pa_status_string, pa_store_kv,
-                      pa_decode_num_partitions, pa_decode_split, pa_decode_reduce)
+                      pa_decode_num_partitions, pa_decode_split, pa_decode_reduce,
+                      pa_decode_store)
 
 __all__ = ["PaError", "library_path", "load", "pa_store_kv", "pa_prefill_varlen", "pa_decode",
            "pa_decode_workspace_size", "pa_decode_num_partitions", "pa_decode_split",
-           "pa_decode_reduce", "pa_slot_mapping",
+           "pa_decode_reduce", "pa_decode_store", "pa_slot_mapping",
            "pa_status_string"]

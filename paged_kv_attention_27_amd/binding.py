@@ -59,6 +59,9 @@ def load():
         fn.restype = ctypes.c_int
         fn.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                        _I, _P, _SZ, _P, _P]
+    lib.pa_decode_store.restype = ctypes.c_int
+    lib.pa_decode_store.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
+                                    _I, ctypes.c_float, _I, _P, _SZ, _P, _P]
     _LIB = lib
     return lib
 
@@ -172,6 +175,32 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
         bs, float(scale), int(partition_size), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(out, torch.bfloat16, "out"), _stream(stream))
     _check(_entry, st)
+    return out
+
+
+def pa_decode_store(q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, context_lens,
+                    max_context_len, scale, workspace=None, out=None, partition_size=0,
+                    stream=None):
+    """Fused decode step: store each sequence's new K/V at its slot and attend (include/pa.h)."""
+    S, Hq, d = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    if tuple(k_new.shape) != (S, Hkv, d) or tuple(v_new.shape) != (S, Hkv, d) \
+            or tuple(slot_mapping.shape) != (S,):
+        raise ValueError("pa_decode_store: inconsistent shapes")
+    if out is None:
+        out = torch.empty_like(q)
+    need = pa_decode_workspace_size(S, Hq, Hkv, d, max_context_len, partition_size)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load().pa_decode_store(
+        _dev(q, torch.bfloat16, "q"), _dev(k_new, torch.bfloat16, "k_new"),
+        _dev(v_new, torch.bfloat16, "v_new"), _dev(slot_mapping, torch.int32, "slot_mapping"),
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens"), S, int(max_context_len), Hq, Hkv, d,
+        bs, float(scale), int(partition_size), _dev(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _dev(out, torch.bfloat16, "out"), _stream(stream))
+    _check("pa_decode_store", st)
     return out
 
 

@@ -18,8 +18,12 @@
 //     max (rescale only when it grows by more than 2^8).  Each wave keeps its
 //     own running max/sum/output; the four waves are merged in LDS.
 //   * If a sequence fits in one partition, that workgroup writes the final
-//     bf16 output; otherwise it writes the partition's running max, sum and
-//     unnormalised output row (fp32) to the workspace and
+//     bf16 output (an empty context writes a zero row); otherwise it writes
+//     the partition's running max, sum and unnormalised output row (fp32) to
+//     the workspace and
+//   * with the fused store, the workgroup holding position ctx-1 takes the new
+//     token's K/V from the caller's rows, writes them to their pool slot, and
+//     attends to them from registers (no separate store launch, no re-read);
 //   * decode_reduce_kernel merges a sequence's partitions with the usual
 //     log-sum-exp rescaling: M = max m_p, L = sum 2^(m_p - M) l_p,
 //     o = sum 2^(m_p - M) o_p / L.
@@ -35,7 +39,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr float kLazyTau = 8.0f;   // log2 growth of a running max tolerated before rescaling
 
-template <int G, int U, bool CHUNK_IN_BLOCK>
+template <int G, int U, bool CHUNK_IN_BLOCK, bool FUSED_STORE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 {
     const int p = blockIdx.x;
@@ -44,10 +48,22 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     const int ctx = a.context_lens[s];
     const int P = a.part_tokens;
     const int t_begin = p * P;
-    if (t_begin >= ctx)
+    if (t_begin >= ctx) {
+        if (ctx <= 0 && p == 0) {   // empty context: a zero output row, defined by the C-ABI
+            uint16_t *out = static_cast<uint16_t *>(a.out) + ((int64_t)s * a.num_q_heads + kvh * G) * D;
+            for (int i = threadIdx.x; i < G * D; i += kThreads)
+                out[i] = 0;
+        }
         return;
+    }
     const int t_end = min(ctx, t_begin + P);
     const int n_part_s = (ctx + P - 1) / P;
+    // fused store: the partition holding position ctx-1 takes the new token's K/V
+    // from k_new/v_new (and writes it to its slot) instead of reading the pool
+    int new_slot = -1;
+    if (FUSED_STORE && t_end == ctx)
+        new_slot = a.slot_mapping[s];
+    const int t_stop = new_slot >= 0 ? ctx - 1 : t_end;   // keys read from the pool
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -86,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     const float sl2 = a.scale_log2;
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
     constexpr int kChunk = 4 * U;   // keys per wave iteration (lane group r owns U consecutive keys)
-    const int n_chunks = (t_end - t_begin + kChunk - 1) / kChunk;
+    const int n_chunks = (t_stop - t_begin + kChunk - 1) / kChunk;
     const int64_t lane_off = (int64_t)(r * U) * row_elems + kvh * D + 8 * c;
 
     for (int ch = wave; ch < n_chunks; ch += kWaves) {
@@ -101,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
             const bf16 *vb = vc + row0 * row_elems + lane_off;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const bool ok = base + u < t_end;
+                const bool ok = base + u < t_stop;
                 kr[u] = ok ? *reinterpret_cast<const uint4 *>(kb + u * row_elems) : make_uint4(0, 0, 0, 0);
                 vr[u] = ok ? *reinterpret_cast<const uint4 *>(vb + u * row_elems) : make_uint4(0, 0, 0, 0);
             }
@@ -109,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int j = base + u;
-                if (j < t_end) {
+                if (j < t_stop) {
                     const int lb = shift >= 0 ? (j >> shift) : (j / bs);
                     const int64_t off = ((int64_t)bt_row[lb] * bs + (j - lb * bs)) * row_elems + kvh * D + 8 * c;
                     kr[u] = *reinterpret_cast<const uint4 *>(kc + off);
@@ -125,7 +141,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
         float sc[G][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const bool valid = base + u < t_end;
+            const bool valid = base + u < t_stop;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float d0 = 0.f;
@@ -191,6 +207,36 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
                                                                         acc[h][2 * w + 1], false);
                 }
             }
+        }
+    }
+
+    if (FUSED_STORE && new_slot >= 0 && wave == 0) {
+        // the new token: K/V from k_new/v_new, stored to its slot by lane group 0
+        const int64_t src = ((int64_t)s * Hkv + kvh) * D + 8 * c;
+        const uint4 kn = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(a.k_new) + src);
+        const uint4 vn = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(a.v_new) + src);
+        if (r == 0) {
+            const int64_t dst = ((int64_t)new_slot * Hkv + kvh) * D + 8 * c;
+            *reinterpret_cast<uint4 *>(static_cast<bf16 *>(const_cast<void *>(a.k_cache)) + dst) = kn;
+            *reinterpret_cast<uint4 *>(static_cast<bf16 *>(const_cast<void *>(a.v_cache)) + dst) = vn;
+        }
+        const float vf[8] = {bf16_lo(vn.x), bf16_hi(vn.x), bf16_lo(vn.y), bf16_hi(vn.y),
+                             bf16_lo(vn.z), bf16_hi(vn.z), bf16_lo(vn.w), bf16_hi(vn.w)};
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            float d0 = 0.f;
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][0]), __builtin_bit_cast(bf16x2, kn.x), d0, false);
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][1]), __builtin_bit_cast(bf16x2, kn.y), d0, false);
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][2]), __builtin_bit_cast(bf16x2, kn.z), d0, false);
+            d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][3]), __builtin_bit_cast(bf16x2, kn.w), d0, false);
+            const float sc_new = row16_sum(d0) * sl2;     // identical in all four lane groups
+            const float mnew = fmaxf(m[h], sc_new);
+            const float alpha = fast_exp2(m[h] - mnew);
+            m[h] = mnew;
+            const float pw = r == 0 ? fast_exp2(sc_new - mnew) : 0.f;   // counted once
+            l[h] = fmaf(l[h], alpha, pw);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(acc[h][e], alpha, pw * vf[e]);
         }
     }
 
@@ -304,21 +350,31 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArg
         *out = f32_to_bf16_bits(o / L);
 }
 
+template <int G, int U, bool FUSED>
+void launch_split(const DecodeArgs &a, hipStream_t stream)
+{
+    dim3 grid(a.n_part, a.num_kv_heads, a.num_seqs);
+    // one table lookup per iteration needs every 4U-key chunk inside one block
+    if (a.block_size % (4 * U) == 0 && a.part_tokens % (4 * U) == 0)
+        hipLaunchKernelGGL((decode_split_kernel<G, U, true, FUSED>), grid, dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<G, U, false, FUSED>), grid, dim3(kThreads), 0, stream, a);
+}
+
 template <int G, int U>
 hipError_t launch_g(const DecodeArgs &a, int passes, hipStream_t stream)
 {
     if (passes & 1) {
-        dim3 grid(a.n_part, a.num_kv_heads, a.num_seqs);
-        // one table lookup per iteration needs every 4U-key chunk inside one block
-        if (a.block_size % (4 * U) == 0 && a.part_tokens % (4 * U) == 0)
-            hipLaunchKernelGGL((decode_split_kernel<G, U, true>), grid, dim3(kThreads), 0, stream, a);
+        if (a.slot_mapping)
+            launch_split<G, U, true>(a, stream);
         else
-            hipLaunchKernelGGL((decode_split_kernel<G, U, false>), grid, dim3(kThreads), 0, stream, a);
+            launch_split<G, U, false>(a, stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
     }
-    if (passes & 2) {
+    // with a single partition every row (empty contexts included) is final
+    if ((passes & 2) && a.n_part > 1) {
         hipLaunchKernelGGL(decode_reduce_kernel, dim3((a.num_q_heads + 1) / 2, a.num_seqs),
                            dim3(kReduceThreads), 0, stream, a);
         return hipGetLastError();

@@ -211,7 +211,8 @@ int decode_passes(const void *q, const void *k_cache, const void *v_cache,
                   const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                   float scale, int32_t partition_size, void *workspace, size_t workspace_bytes,
-                  void *out, hipStream_t stream, int passes)
+                  void *out, hipStream_t stream, int passes, const void *k_new = nullptr,
+                  const void *v_new = nullptr, const int32_t *slot_mapping = nullptr)
 {
     if (num_seqs < 0 || max_context_len < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
         head_dim < 1 || block_size < 1 || max_blocks_per_seq < 1 ||
@@ -244,6 +245,9 @@ int decode_passes(const void *q, const void *k_cache, const void *v_cache,
 
     pa::DecodeArgs a;
     a.q = q;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.slot_mapping = slot_mapping;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
     a.block_tables = block_tables;
@@ -280,6 +284,24 @@ extern "C" {
         partition_size, workspace, workspace_bytes, out, stream
 
 int pa_decode(PA_DECODE_ARGS) { return decode_passes(PA_DECODE_FWD, 3); }
+
+int pa_decode_store(const void *q, const void *k_new, const void *v_new,
+                    const int32_t *slot_mapping, void *k_cache, void *v_cache,
+                    const int32_t *block_tables, int32_t max_blocks_per_seq,
+                    const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, float scale, int32_t partition_size, void *workspace,
+                    size_t workspace_bytes, void *out, hipStream_t stream)
+{
+    if (num_seqs > 0 && (!k_new || !v_new || !slot_mapping))
+        return PA_ERR_NULL;
+    if (!aligned16(k_new) || !aligned16(v_new))
+        return PA_ERR_UNSUPPORTED;
+    return decode_passes(q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                         num_seqs, max_context_len, num_q_heads, num_kv_heads, head_dim,
+                         block_size, scale, partition_size, workspace, workspace_bytes, out,
+                         stream, 3, k_new, v_new, slot_mapping);
+}
 int pa_decode_split(PA_DECODE_ARGS) { return decode_passes(PA_DECODE_FWD, 1); }
 int pa_decode_reduce(PA_DECODE_ARGS) { return decode_passes(PA_DECODE_FWD, 2); }
 

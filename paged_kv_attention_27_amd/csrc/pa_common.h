@@ -60,6 +60,9 @@ hipError_t launch_store_kv(const void *k, const void *v, void *k_cache, void *v_
 
 struct DecodeArgs {
     const void *q;
+    const void *k_new;            // fused store: new token rows [S, Hkv, D] (or null)
+    const void *v_new;
+    const int32_t *slot_mapping;  // fused store: pool row of each sequence's new token
     const void *k_cache;
     const void *v_cache;
     const int32_t *block_tables;

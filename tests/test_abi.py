@@ -116,6 +116,22 @@ def test_decode_validation(lib):
     assert _decode(lib, S=0, q=None) == OK
 
 
+def test_decode_store_validation(lib):
+    st = lib.pa_decode_store
+    args = [FAKE, FAKE, FAKE, FAKE2, FAKE, FAKE, FAKE2, 16, FAKE2, 4, 4096, 16, 8, 128, 256,
+            ctypes.c_float(0.088), 0, FAKE, 1 << 30, FAKE, None]
+    a = list(args); a[1] = None
+    assert st(*a) == NULL                                   # k_new required
+    a = list(args); a[3] = None
+    assert st(*a) == NULL                                   # slot_mapping required
+    a = list(args); a[2] = ctypes.c_void_p(0x10008)
+    assert st(*a) == UNSUPPORTED                            # v_new not 16-byte aligned
+    a = list(args); a[18] = 10
+    assert st(*a) == WORKSPACE
+    a = list(args); a[9] = 0; a[1] = a[2] = a[3] = None
+    assert st(*a) == OK                                     # no sequences: nothing to do
+
+
 def test_decode_sizes(lib):
     np_ = lib.pa_decode_num_partitions
     assert np_(256, 8, 4096, 512) == 8

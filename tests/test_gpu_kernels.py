@@ -230,3 +230,67 @@ def test_decode_empty_context_gives_zeros(pa):
     ctx = dev_i32(np.array([0, 0, 0], np.int32))
     out = pa.pa_decode(q, dev_bf16(pool), dev_bf16(pool), bt, ctx, 0, 0.088)
     assert (host_u16(out) == 0).all()
+
+
+# ------------------------------------------------------------------ fused store + decode
+
+def _fused_case(pa, orc, wl, label, partition_size=0, skip_store=()):
+    """pa_decode_store on a one-token-per-sequence problem vs the oracle's store + decode.
+
+    Sequences listed in ``skip_store`` get slot -1: their new token is stored
+    beforehand with pa_store_kv, so the fused call must read it from the pool.
+    """
+    ph = wl.prefill
+    bs = wl.block_size
+    kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
+    okc, ovc = wl.k_cache.copy(), wl.v_cache.copy()
+    fx = wl.prefix
+    if fx is not None:
+        slots = pa.pa_slot_mapping(fx.cu_seqlens_q, fx.seqlens_k, prefix_tables(wl), bs)
+        pa.pa_store_kv(dev_bf16(fx.k), dev_bf16(fx.v), kc, vc, slots.cuda())
+        orc.store(fx.k, fx.v, orc.slot_mapping(fx.cu_seqlens_q, fx.seqlens_k, prefix_tables(wl), bs),
+                  okc, ovc)
+    slots = pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, bs)
+    if skip_store:
+        pre = slots.clone()
+        keep = np.ones(len(pre), bool)
+        keep[list(skip_store)] = False
+        pre[torch.from_numpy(keep)] = -1
+        pa.pa_store_kv(dev_bf16(ph.k), dev_bf16(ph.v), kc, vc, pre.cuda())
+        slots[list(skip_store)] = -1
+    out = pa.pa_decode_store(dev_bf16(ph.q), dev_bf16(ph.k), dev_bf16(ph.v), slots.cuda(), kc, vc,
+                             dev_i32(wl.block_tables), dev_i32(ph.seqlens_k), int(ph.seqlens_k.max()),
+                             wl.scale, partition_size=partition_size)
+    orc.store(ph.k, ph.v, orc.slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, bs),
+              okc, ovc)
+    ref = orc.decode(ph.q, okc, ovc, wl.block_tables, ph.seqlens_k, wl.scale)
+    log(f"[{label}]")
+    assert np.array_equal(host_u16(kc), okc) and np.array_equal(host_u16(vc), ovc), "pools differ"
+    check_close(host_f64(out), ref, label)
+    return out
+
+
+@pytest.mark.parametrize("part", [0, 32, 96, 512, 4096])
+def test_decode_store_fused_partitions(pa, orc, part):
+    wl = _wl(q_lens=[1] * len(CTX), k_lens=CTX, seed=41, q_scale=2.0)
+    _fused_case(pa, orc, wl, f"fused partition={part}", partition_size=part)
+
+
+@pytest.mark.parametrize("bs", [1, 16, 256, 768])
+def test_decode_store_fused_block_sizes(pa, orc, bs):
+    wl = _wl(q_lens=[1] * 5, k_lens=[1, 2, 300, 769, 1537], block_size=bs, seed=42, q_scale=4.0,
+             v_position=True)
+    _fused_case(pa, orc, wl, f"fused bs={bs}")
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 1), (16, 8), (32, 8)])
+def test_decode_store_fused_groups(pa, orc, hq, hkv):
+    wl = _wl(q_lens=[1] * 4, k_lens=[1, 600, 1300, 2000], num_q_heads=hq, num_kv_heads=hkv,
+             seed=43, q_scale=8.0)
+    _fused_case(pa, orc, wl, f"fused Hq={hq} Hkv={hkv}")
+
+
+def test_decode_store_fused_negative_slot_reads_pool(pa, orc):
+    """A negative slot skips the fused store; the token already in the pool is used."""
+    wl = _wl(q_lens=[1] * 4, k_lens=[5, 257, 1000, 64], seed=44, q_scale=3.0)
+    _fused_case(pa, orc, wl, "fused negative slots", skip_store=(1, 3))
