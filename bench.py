@@ -17,7 +17,9 @@ The same run also measures, as sub-objects of the JSON line:
   * ``prefill``: the varlen prefill round (store + attention) on the 8-sequence
     no-cache batch and on the 16-sequence prefix-cache batch, in TFLOP/s of
     algorithmic work (two GEMMs over visible query/key pairs only);
-  * ``decode_long``: the 16 x 32768-token decode (Hq=32, group of 4).
+  * ``decode_long``: the 16 x 32768-token decode (Hq=32, group of 4);
+  * ``decode_head_ratios``: the 256-sequence decode at 8 Q heads over 8, 2
+    and 1 KV heads (MHA, GQA, MQA: KV bytes 8:2:1).
 ``roofline`` is the dominant kernel of the headline step (the split-K decode
 pass with the fused store), timed alone with HIP events on its own stream;
 ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of the same
@@ -359,6 +361,23 @@ def main():
         log(f"long decode: {l_ms * 1e3:.1f} us/step, split {l_split * 1e3:.1f} us")
         del ls, lwl
         torch.cuda.empty_cache()
+
+        # MHA / GQA / MQA at 8 Q heads: KV bytes 8:2:1 for the same lengths
+        ratios = {}
+        for hkv in (8, 2, 1):
+            hwl = workloads.head_ratio_decode(hkv)
+            hs = DecodeSetup(torch, pa, hwl, args.partition)
+            hs.capture()
+            h_ms, _ = hs.time_steps(max(args.steps // 2, 5), args.warmup)
+            ratios[hwl.name] = {"num_kv_heads": hkv, "kv_bytes": hs.bytes,
+                                "ms_per_step": round(h_ms, 5), "num_partitions": hs.n_part,
+                                "value": round(hs.bytes / (h_ms * 1e-3) / 1e9, 2), "unit": "GB/s"}
+            log(f"Hq8/Hkv{hkv}: {h_ms * 1e3:.1f} us/step, {hs.bytes / (h_ms * 1e-3) / 1e9:.0f} GB/s")
+            del hs, hwl
+            torch.cuda.empty_cache()
+        result["decode_head_ratios"] = {
+            "workload": "256 seqs, ctx U[128,4096], Hq 8 over Hkv 8/2/1, block 256; fused step, HIP graph",
+            **ratios}
 
     if args.calibrate_copy:
         n = 1 << 29   # bf16 elements: 1 GiB read + 1 GiB written per copy

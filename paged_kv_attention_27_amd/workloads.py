@@ -278,6 +278,22 @@ def config5(seed: int = 27005, values: bool = True) -> Workload:
                           streams, ctx, 32, 8, 128, 256, 2048, values)
 
 
+def head_ratio_decode(num_kv_heads: int, seed: int = 27010, values: bool = True) -> Workload:
+    """256-sequence decode with 8 Q heads over 8, 2 or 1 KV heads (MHA, GQA, MQA).
+
+    Same lengths (ctx U[128,4096]) and values stream for every ratio, so the KV
+    bytes read scale 8:2:1 ("Visual atlas" ch.18: with Q heads fixed at 8, the
+    KV capacity of MHA, GQA and MQA is 8:2:1).
+    """
+    streams = _streams(seed)
+    ctx = streams[0].integers(128, 4096, size=256, endpoint=True).astype(np.int32)
+    name = {8: "mha", 2: "gqa", 1: "mqa"}.get(num_kv_heads, f"hkv{num_kv_heads}")
+    return _decode_config(f"decode_hq8_{name}",
+                          f"256 seqs, ctx~U[128,4096], Hq8/Hkv{num_kv_heads}/d128, bs256, "
+                          "4096-block pool; store new K/V then paged decode",
+                          streams, ctx, 8, num_kv_heads, 128, 256, 4096, values)
+
+
 def _scale(d: int) -> float:
     # 1/sqrt(d) as the float32 both sides receive
     return float(np.float32(1.0 / math.sqrt(d)))

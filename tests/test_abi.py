@@ -181,3 +181,15 @@ def test_binding_refuses_missing_library(monkeypatch):
     monkeypatch.setenv("PA_LIBRARY", "/nonexistent/libpa.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         binding.load()
+
+
+def test_graph_bucket_choice():
+    from paged_kv_attention_27_amd.decode_graphs import DEFAULT_BUCKETS, bucket_for
+    assert bucket_for(1, DEFAULT_BUCKETS) == 1
+    assert bucket_for(3, DEFAULT_BUCKETS) == 4
+    assert bucket_for(17, (16, 1, 64)) == 64
+    assert bucket_for(256, DEFAULT_BUCKETS) == 256
+    with pytest.raises(ValueError):
+        bucket_for(257, DEFAULT_BUCKETS)
+    with pytest.raises(ValueError):
+        bucket_for(0, DEFAULT_BUCKETS)

@@ -64,3 +64,26 @@ def test_config_decode_fused(cfg, orc):
     assert np.array_equal(host_u16(kc), okc) and np.array_equal(host_u16(vc), ovc)
     ref = orc.decode(ph.q, okc, ovc, wl.block_tables, ph.seqlens_k, wl.scale)
     check_close(got, ref, f"config {cfg} fused decode")
+
+
+@pytest.mark.parametrize("hkv", [8, 2, 1], ids=["mha", "gqa", "mqa"])
+def test_head_ratio_decode_parity(hkv, orc):
+    """Hq = 8 over Hkv = 8 / 2 / 1 at the batched-decode size (fused step vs oracle)."""
+    import paged_kv_attention_27_amd as pa
+    from paged_kv_attention_27_amd import workloads
+    from pipelines import dev_bf16, dev_i32, host_f64, host_u16
+    log(f"[Hq8/Hkv{hkv}] generating inputs")
+    wl = workloads.head_ratio_decode(hkv)
+    kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
+    okc, ovc = wl.k_cache.copy(), wl.v_cache.copy()
+    ph = wl.decode
+    slots = pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, wl.block_size)
+    out = pa.pa_decode_store(dev_bf16(ph.q), dev_bf16(ph.k), dev_bf16(ph.v), slots.cuda(), kc, vc,
+                             dev_i32(wl.block_tables), dev_i32(ph.seqlens_k), ph.max_seqlen_k,
+                             wl.scale)
+    got = host_f64(out)
+    orc.store(ph.k, ph.v, orc.slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables,
+                                           wl.block_size), okc, ovc)
+    assert np.array_equal(host_u16(kc), okc) and np.array_equal(host_u16(vc), ovc)
+    ref = orc.decode(ph.q, okc, ovc, wl.block_tables, ph.seqlens_k, wl.scale)
+    check_close(got, ref, f"Hq8/Hkv{hkv} fused decode")
