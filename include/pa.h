@@ -181,9 +181,9 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * workspace     (device) >= pa_decode_workspace_size(...) bytes, any content
  * out           (device, out) [num_seqs, num_q_heads, head_dim] bf16
  * partition_size  0 (library's choice: one partition per sequence when
- *               num_seqs * num_kv_heads >= 2048, else a multiple of 256 keys that
- *               makes num_seqs * num_kv_heads * partitions about 4096) or a
- *               multiple of 32 tokens
+ *               num_seqs * num_kv_heads >= 512, else a multiple of 256 keys, at
+ *               least 1024, that makes num_seqs * num_kv_heads * partitions
+ *               about 4096) or a multiple of 32 tokens
  * Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
  */
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,

@@ -12,7 +12,8 @@ namespace {
 
 constexpr int kHeadDim = 128;
 constexpr int64_t kDecodeTargetWorkgroups = 4096;   // ~16 per CU on 256 CUs
-constexpr int64_t kDecodeWholeSequencePairs = 2048;  // (sequence, KV head) pairs that fill the chip
+constexpr int64_t kDecodeWholeSequencePairs = 512;   // (sequence, KV head) pairs that fill the chip
+constexpr int64_t kDecodeMinPartition = 1024;        // keys: below this, per-workgroup overhead dominates
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -31,20 +32,24 @@ bool group_supported(int32_t hq, int32_t hkv) {
     return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
-// Library's decode partition size (host integers only).  With at least 2048
-// (sequence, KV head) pairs every sequence is one partition: the grid already
-// fills the chip, and whole-sequence workgroups need no partials or merge.
-// Otherwise the context is split so the grid holds about 4096 workgroups,
-// in multiples of 256 keys.
+// Library's decode partition size (host integers only), tuned on MI355X.
+// With at least 512 (sequence, KV head) pairs every sequence is one
+// partition: the grid already fills the chip, and whole-sequence workgroups
+// need no partials or merge.  Otherwise the context is split so the grid
+// holds about 4096 workgroups, but never into partitions under 1024 keys,
+// where each workgroup's fixed cost (query load, four-wave merge, partial
+// write) outweighs its streaming time.  Multiples of 256 keys.
 int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
                           int32_t max_context_len) {
     if (partition_size != 0)
         return partition_size;
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-    int64_t n_part = 1;
-    if (pairs > 0 && pairs < kDecodeWholeSequencePairs)
-        n_part = (kDecodeTargetWorkgroups + pairs - 1) / pairs;
-    int64_t part = ((int64_t)max_context_len + n_part - 1) / n_part;
+    int64_t part = max_context_len;
+    if (pairs > 0 && pairs < kDecodeWholeSequencePairs) {
+        part = ((int64_t)max_context_len * pairs + kDecodeTargetWorkgroups - 1) / kDecodeTargetWorkgroups;
+        if (part < kDecodeMinPartition)
+            part = kDecodeMinPartition;
+    }
     part = (part + 255) / 256 * 256;
     if (part < 256)
         part = 256;

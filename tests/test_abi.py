@@ -141,10 +141,12 @@ def test_decode_sizes(lib):
     assert np_(4, 8, 100, 33) == 0
     assert lib.pa_decode_workspace_size(3, 16, 8, 128, 1000, 256) == 3 * 16 * 4 * 130 * 4
     assert np_(256, 8, 4096, 0) == 1      # auto: 2048 pairs fill the chip, one partition
+    assert np_(256, 2, 4096, 0) == 1      # auto: 512 pairs, one partition
+    assert np_(256, 1, 4096, 0) == 4      # auto: 256 pairs, 1024-key partitions
     assert np_(16, 8, 32768, 0) == 32     # auto: 1024-key partitions, 4096 workgroups
-    assert np_(4, 8, 512, 0) == 2         # auto: at least 256 keys
+    assert np_(4, 8, 512, 0) == 1         # auto: at least 1024 keys
     assert np_(1, 8, 10**6, 0) == 489     # auto: 1954 keys, rounded up to 2048
-    assert np_(1, 1, 1000, 0) == 4        # auto: rounded up to 256 keys
+    assert np_(1, 1, 3000, 0) == 3        # auto: 1024-key minimum
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
