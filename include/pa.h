@@ -242,6 +242,83 @@ int pa_decode_reduce(const void *q, const void *k_cache, const void *v_cache,
                      int32_t block_size, float scale, int32_t partition_size,
                      void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
 
+/*
+ * Host block manager with prefix caching.
+ *
+ * Owns the ids of a pool of num_blocks physical blocks (the pools themselves
+ * stay the caller's device buffers) and hands them to sequences as block
+ * tables.  The pool is reserved once; allocating and freeing only change
+ * which ids a sequence holds ([Course] "THE IMPORTANT DETAILS" item 02).  It
+ * keeps, per block, a reference count and, for a full block, a prefix key
+ * ([Notes] "key state and module boundaries").
+ *
+ * Sharing rule ([Course] "ACCURACY & SCOPE"; [Atlas] ch.25, ch.28 captions):
+ * only full blocks are shared, never the trailing partial block.  A full
+ * block's key chains the key of the block before it, a caller salt (say, a
+ * model or adapter id: requests with different salts never share), and its
+ * tokens; a candidate hit is confirmed by comparing the stored tokens, so a
+ * hash collision cannot share wrong data.  Once one block of a request
+ * misses, every later block is fresh.  A block whose count drops to zero keeps
+ * its key and content and can still be hit until it is handed out fresh;
+ * fresh blocks are taken least-recently-freed first.
+ *
+ * The manager touches no GPU state and is not thread-safe: one thread (the
+ * scheduler) owns a manager.  Token ids are opaque int32 values.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager over num_blocks blocks of block_size tokens (all free), or NULL
+ * when a size is < 1 or memory runs out.  Release with pa_bm_destroy. */
+pa_block_manager *pa_bm_create(int32_t num_blocks, int32_t block_size);
+void pa_bm_destroy(pa_block_manager *bm);
+
+/* Blocks with reference count 0 (cached or not); -1 for NULL. */
+int32_t pa_bm_num_free(const pa_block_manager *bm);
+
+/* Reference count of one block id; -1 for NULL or an id out of range. */
+int32_t pa_bm_ref_count(const pa_block_manager *bm, int32_t block);
+
+/* Free blocks pa_bm_allocate would take for this prompt now (a hit on a free
+ * cached block counts, since it leaves the free pool); -1 on bad arguments. */
+int32_t pa_bm_blocks_needed(const pa_block_manager *bm, const int32_t *tokens,
+                            int32_t num_tokens, uint64_t salt);
+
+/*
+ * Block table for a new request whose prompt is tokens[0 .. num_tokens-1]
+ * (all host memory).  Entries 0 .. ceil(num_tokens/block_size)-1 of
+ * block_table [max_blocks] receive block ids, the rest -1.
+ * *num_cached_tokens receives the length of the shared prefix (a multiple of
+ * block_size): those positions already hold this prompt's K/V, so the prefill
+ * stores and attends only positions from there on ([Atlas] ch.26: after a
+ * prefix hit, the query covers the uncached tail and the keys the whole
+ * prompt).  The block holding the last prompt token is never taken from the
+ * cache, so num_cached_tokens < num_tokens for any non-empty prompt: the
+ * prefill has at least one query row and writes only blocks that this request
+ * holds alone.  Returns PA_ERR_WORKSPACE,
+ * taking nothing, when fewer than pa_bm_blocks_needed blocks are free;
+ * PA_ERR_SHAPE when the table is too short.
+ */
+int pa_bm_allocate(pa_block_manager *bm, const int32_t *tokens, int32_t num_tokens,
+                   uint64_t salt, int32_t *block_table, int32_t max_blocks,
+                   int32_t *num_cached_tokens);
+
+/*
+ * One decode step of a running sequence: tokens[0 .. num_tokens-1] is its whole
+ * token list including the token being appended (position num_tokens-1).
+ * When that position opens a new block, a fresh block is taken into
+ * block_table (PA_ERR_WORKSPACE, nothing changed, if none is free); when it
+ * fills a block, that block is registered for later prefix hits.  Returns
+ * PA_ERR_SHAPE for a table too short or inconsistent with num_tokens.
+ */
+int pa_bm_append(pa_block_manager *bm, const int32_t *tokens, int32_t num_tokens,
+                 uint64_t salt, int32_t *block_table, int32_t max_blocks);
+
+/* Release a finished (or preempted) sequence's blocks: every id >= 0 among
+ * block_table[0 .. num_blocks-1] loses one reference; blocks reaching zero
+ * become free (most recent last).  PA_ERR_SHAPE for an id out of range or not
+ * held; entries before it in reverse order may already have been released. */
+int pa_bm_free(pa_block_manager *bm, const int32_t *block_table, int32_t num_blocks);
+
 #ifdef __cplusplus
 }
 #endif

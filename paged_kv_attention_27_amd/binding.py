@@ -62,6 +62,23 @@ def load():
     lib.pa_decode_store.restype = ctypes.c_int
     lib.pa_decode_store.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                     _I, ctypes.c_float, _I, _P, _SZ, _P, _P]
+    _U64 = ctypes.c_uint64
+    lib.pa_bm_create.restype = _P
+    lib.pa_bm_create.argtypes = [_I, _I]
+    lib.pa_bm_destroy.restype = None
+    lib.pa_bm_destroy.argtypes = [_P]
+    lib.pa_bm_num_free.restype = _I
+    lib.pa_bm_num_free.argtypes = [_P]
+    lib.pa_bm_ref_count.restype = _I
+    lib.pa_bm_ref_count.argtypes = [_P, _I]
+    lib.pa_bm_blocks_needed.restype = _I
+    lib.pa_bm_blocks_needed.argtypes = [_P, _P, _I, _U64]
+    lib.pa_bm_allocate.restype = ctypes.c_int
+    lib.pa_bm_allocate.argtypes = [_P, _P, _I, _U64, _P, _I, _P]
+    lib.pa_bm_append.restype = ctypes.c_int
+    lib.pa_bm_append.argtypes = [_P, _P, _I, _U64, _P, _I]
+    lib.pa_bm_free.restype = ctypes.c_int
+    lib.pa_bm_free.argtypes = [_P, _P, _I]
     _LIB = lib
     return lib
 
@@ -216,3 +233,101 @@ def pa_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, max_contex
     """Reduce pass of pa_decode (same arguments); see include/pa.h."""
     return pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                      workspace, out, partition_size, stream, _entry="pa_decode_reduce")
+
+
+# ---------------------------------------------------------------------------
+# Host block manager (pa_bm_*): all arguments are host memory.
+
+def _host_i32(x):
+    t = torch.as_tensor(x, dtype=torch.int32)
+    if t.device.type != "cpu":
+        raise TypeError("block manager arguments are host (CPU) int32 data")
+    return t.contiguous()
+
+
+def pa_bm_create(num_blocks, block_size):
+    h = load().pa_bm_create(int(num_blocks), int(block_size))
+    if not h:
+        raise ValueError(f"pa_bm_create({num_blocks}, {block_size}) failed")
+    return h
+
+
+def pa_bm_destroy(bm):
+    load().pa_bm_destroy(bm)
+
+
+def pa_bm_num_free(bm):
+    return load().pa_bm_num_free(bm)
+
+
+def pa_bm_ref_count(bm, block):
+    return load().pa_bm_ref_count(bm, int(block))
+
+
+def pa_bm_blocks_needed(bm, tokens, salt=0):
+    t = _host_i32(tokens)
+    return load().pa_bm_blocks_needed(bm, t.data_ptr(), t.numel(), int(salt))
+
+
+def pa_bm_allocate(bm, tokens, max_blocks, salt=0):
+    """Returns (block_table int32 CPU tensor [max_blocks], num_cached_tokens)."""
+    t = _host_i32(tokens)
+    table = torch.empty(int(max_blocks), dtype=torch.int32)
+    cached = ctypes.c_int32(0)
+    _check("pa_bm_allocate", load().pa_bm_allocate(bm, t.data_ptr(), t.numel(), int(salt),
+                                                   table.data_ptr(), table.numel(),
+                                                   ctypes.byref(cached)))
+    return table, cached.value
+
+
+def pa_bm_append(bm, tokens, block_table, salt=0):
+    """Updates block_table (a contiguous int32 CPU tensor) in place."""
+    t = _host_i32(tokens)
+    if block_table.dtype != torch.int32 or block_table.device.type != "cpu" \
+            or not block_table.is_contiguous():
+        raise TypeError("block_table: expected a contiguous int32 CPU tensor")
+    _check("pa_bm_append", load().pa_bm_append(bm, t.data_ptr(), t.numel(), int(salt),
+                                               block_table.data_ptr(), block_table.numel()))
+
+
+def pa_bm_free(bm, block_table):
+    bt = _host_i32(block_table)
+    _check("pa_bm_free", load().pa_bm_free(bm, bt.data_ptr(), bt.numel()))
+
+
+class BlockManager:
+    """Owning handle over a pa_block_manager (see pa_bm_create)."""
+
+    def __init__(self, num_blocks, block_size):
+        self.block_size = int(block_size)
+        self.num_blocks = int(num_blocks)
+        self._h = pa_bm_create(num_blocks, block_size)
+
+    def close(self):
+        if self._h:
+            pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self):
+        return pa_bm_num_free(self._h)
+
+    def ref_count(self, block):
+        return pa_bm_ref_count(self._h, block)
+
+    def blocks_needed(self, tokens, salt=0):
+        return pa_bm_blocks_needed(self._h, tokens, salt)
+
+    def allocate(self, tokens, max_blocks, salt=0):
+        return pa_bm_allocate(self._h, tokens, max_blocks, salt)
+
+    def append(self, tokens, block_table, salt=0):
+        pa_bm_append(self._h, tokens, block_table, salt)
+
+    def free(self, block_table):
+        pa_bm_free(self._h, block_table)
