@@ -22,28 +22,37 @@
 // consecutive k-indices, which matches once bits 2 and 3 of the key index are
 // swapped.  The two transposing reads fetch exactly that key order for V^T, so
 // P^T needs no shuffle.  Softmax statistics are per lane (one column), with one
-// cross-half exchange per tile.  The running maximum is updated lazily: the
-// output is rescaled only when a column's maximum grows by more than 2^8, so
-// weights stay <= 256 and most tiles skip the rescale entirely.
+// cross-half exchange (v_permlane32_swap) per tile.  The running maximum is
+// updated lazily: the output is rescaled only when a column's maximum grows by
+// more than 2^8, so weights stay <= 256 and most tiles skip the rescale.
 //
-// K/V tiles of 64 keys are double-buffered in LDS (one barrier per tile) and
-// prefetched into registers two tiles ahead.  Rows past k_len are zero-filled,
-// never read.  When the block size is a multiple of 64 a tile lies inside one
-// block: one table lookup per tile, otherwise one per row.  Heaviest query
-// blocks are dispatched first; blockIdx mod Hkv = KV head keeps every block of a
-// (sequence, KV head) on one XCD so its K/V stays in that L2.
+// K/V tiles of 64 keys go from global memory straight into LDS
+// (global_load_lds_dwordx4: lane i of an instruction fills the i-th 16-byte
+// chunk of a 1 KB span, i.e. 4 tile rows), double-buffered in two LDS stages:
+// the copy of tile t+1 is issued before tile t is computed and waited for at
+// the end of the step, so it overlaps a whole tile of work and costs no
+// registers.  Rows are 256 B with no padding; the 16-byte chunk c of row r is
+// stored at position c ^ swz(r mod 16), swz(r) = 4 (r mod 4) + (r div 4) mod 4,
+// which keeps both the b128 K reads (16 rows, one chunk) and the transposing V
+// reads (4 rows, 2-4 chunks) free of bank conflicts.  Rows past k_len load a
+// copy of the last valid row, so every V value is finite and every key past
+// k_len is removed by the causal mask.  The block tables are read one tile
+// ahead with vector loads.  Heaviest query blocks are dispatched first;
+// blockIdx mod Hkv = KV head keeps every block of a (sequence, KV head) on one
+// XCD so its K/V stays in that L2.
 #include "pa_common.h"
+
+#include <type_traits>
 
 namespace pa {
 namespace {
 
 constexpr int D = 128;
-constexpr int BN = 64;          // keys per tile
+constexpr int BN = 64;             // keys per tile
 constexpr int kThreads = 256;
-constexpr int KST = D + 8;      // K tile row stride (bf16): 272 B, conflict-free b128 reads
-constexpr int VST = D + 32;     // V tile row stride (bf16): 320 B, conflict-free tr reads
-constexpr int KBUF = BN * KST;
-constexpr int VBUF = BN * VST;
+constexpr int ROWB = 2 * D;        // bytes per tile row
+constexpr int TILEB = BN * ROWB;   // 16 KB
+constexpr int STAGEB = 2 * TILEB;  // K tile, then V tile
 constexpr float kLazyTau = 8.0f;   // log2 growth of a column max tolerated before rescaling
 
 enum { kFlat = 0, kPagedTile = 1, kPagedRow = 2 };
@@ -51,40 +60,44 @@ enum { kFlat = 0, kPagedTile = 1, kPagedRow = 2 };
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef short v8i16 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void global_void;
 
-__device__ __forceinline__ bf16x8 read_vt(const bf16 *p0, const bf16 *p1) {
+// position of 16-byte chunk c of tile row r is c ^ swz(r & 15)
+__device__ __forceinline__ int swz(int r16) { return 4 * (r16 & 3) + (r16 >> 2); }
+
+__device__ __forceinline__ bf16x8 read_vt(const char *p0, const char *p1) {
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p0));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16 *)(p1));
     const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, ab);
 }
 
+// value of x held by lane (lane xor 32)
+__device__ __forceinline__ float other_half(float x, int hl) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(hl ? r[0] : r[1]);
+}
+
+// One work item: query block qb (BM = 128/g positions) of sequence s against KV
+// head kvh, through the two LDS stages.  The caller guarantees qb * BM < q_len.
+// Every path through it ends with a workgroup barrier, so items can follow each
+// other on the same stages.
 template <int G, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
+__device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb, int kvh,
+                                             char *stage0, char *stage1)
 {
     constexpr int BM = 128 / G;
-    __shared__ __attribute__((aligned(16))) bf16 k_lds[2 * KBUF];
-    __shared__ __attribute__((aligned(16))) bf16 v_lds[2 * VBUF];
-
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, S = a.num_seqs;
-    const int n_qblk = (a.max_seqlen_q + BM - 1) / BM;
-    int idx = blockIdx.x;
-    const int kvh = idx % Hkv;
-    idx /= Hkv;
-    const int s = idx % S;
-    const int qb = n_qblk - 1 - idx / S;   // heaviest query blocks are dispatched first
-
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const int q0 = a.cu_seqlens_q[s];
     const int q_len = a.cu_seqlens_q[s + 1] - q0;
-    if (qb * BM >= q_len)
-        return;
     const int k0 = a.cu_seqlens_k[s];
     const int k_len = a.cu_seqlens_k[s + 1] - k0;
     const int off = k_len - q_len;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int hl = lane >> 5;        // which half of the MFMA k-range this lane feeds
     const int col = lane & 31;       // this lane's column (query) inside the wave
     const int ccol = wave * 32 + col;
@@ -112,55 +125,67 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const int bs = a.block_size, shift = a.bs_shift;
     const int64_t row_elems = (int64_t)Hkv * D;
 
-    // loader: thread owns rows lrow + 16*ps of each tile, 8 head-dim elements at 8*lchunk
-    const int lrow = tid >> 4;
-    const int lchunk = tid & 15;
-    const int64_t lane_off = (int64_t)lrow * row_elems + kvh * D + 8 * lchunk;
-    uint4 kbuf[4], vbuf[4];
+    // copy mapping: instruction j (0..3) of this wave fills tile rows 16*wave + 4*j + lsub,
+    // lane position lpos of the row; it fetches logical chunk lpos ^ swz(4*j + lsub)
+    const int lsub = lane >> 4;
+    const int lpos = lane & 15;
+    const int n_blk = MODE == kFlat ? 0 : (k_len + bs - 1) / bs;
 
-    auto load_tile = [&](int kt) {
-        const int key0 = kt * BN;
-        if (MODE == kPagedRow) {
+    auto block_of = [&](int key) { return shift >= 0 ? (key >> shift) : (key / bs); };
+    // block-table entries the copy of tile t needs, read into registers one tile ahead
+    auto load_tbl = [&](int t, int32_t (&tbl)[4]) {
+        if (MODE == kPagedTile) {
+            // a tile lies in one block; each lane reads a neighbouring entry (a vector load)
+            // and the copy uses lane 0's
+            tbl[0] = bt_row[min(block_of(t * BN) + lane, n_blk - 1)];
+        } else if (MODE == kPagedRow) {
 #pragma unroll
-            for (int ps = 0; ps < 4; ++ps) {
-                const int key = key0 + lrow + 16 * ps;
-                if (key < k_len) {
-                    const int lb = shift >= 0 ? (key >> shift) : (key / bs);
-                    const int64_t e = ((int64_t)bt_row[lb] * bs + (key - lb * bs)) * row_elems + kvh * D + 8 * lchunk;
-                    kbuf[ps] = *reinterpret_cast<const uint4 *>(ksrc + e);
-                    vbuf[ps] = *reinterpret_cast<const uint4 *>(vsrc + e);
-                } else {
-                    kbuf[ps] = make_uint4(0, 0, 0, 0);
-                    vbuf[ps] = make_uint4(0, 0, 0, 0);
-                }
-            }
-        } else {
-            int64_t base_row;
-            if (MODE == kFlat) {
-                base_row = (int64_t)k0 + key0;
+            for (int j = 0; j < 4; ++j)
+                tbl[j] = bt_row[block_of(min(t * BN + 16 * wave + 4 * j + lsub, k_len - 1))];
+        }
+    };
+    auto issue_tile = [&](char *stage, int t, const int32_t (&tbl)[4]) {
+        const int key0 = t * BN;
+        const int last = k_len - 1 - key0;   // rows past it copy this row
+        int64_t tile_row0 = 0;
+        if (MODE == kFlat) {
+            tile_row0 = (int64_t)k0 + key0;
+        } else if (MODE == kPagedTile) {
+            const int lb = block_of(key0);
+            tile_row0 = (int64_t)__builtin_amdgcn_readfirstlane(tbl[0]) * bs + (key0 - lb * bs);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = min(16 * wave + 4 * j + lsub, last);
+            int64_t row;
+            if (MODE == kPagedRow) {
+                const int key = key0 + r;
+                row = (int64_t)tbl[j] * bs + (key - block_of(key) * bs);
             } else {
-                const int lb = __builtin_amdgcn_readfirstlane(shift >= 0 ? (key0 >> shift) : (key0 / bs));
-                base_row = (int64_t)__builtin_amdgcn_readfirstlane(bt_row[lb]) * bs + (key0 - lb * bs);
+                row = tile_row0 + r;
             }
-            const bf16 *kb = ksrc + base_row * row_elems + lane_off;
-            const bf16 *vb = vsrc + base_row * row_elems + lane_off;
-#pragma unroll
-            for (int ps = 0; ps < 4; ++ps) {
-                const bool ok = key0 + lrow + 16 * ps < k_len;
-                kbuf[ps] = ok ? *reinterpret_cast<const uint4 *>(kb + 16 * ps * row_elems) : make_uint4(0, 0, 0, 0);
-                vbuf[ps] = ok ? *reinterpret_cast<const uint4 *>(vb + 16 * ps * row_elems) : make_uint4(0, 0, 0, 0);
-            }
+            const int64_t e = row * row_elems + kvh * D + 8 * (lpos ^ (4 * lsub + j));
+            char *dst = stage + (16 * wave + 4 * j) * ROWB;
+            __builtin_amdgcn_global_load_lds((global_void *)(ksrc + e), (lds_void *)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((global_void *)(vsrc + e), (lds_void *)(dst + TILEB), 16, 0, 0);
         }
     };
-    auto store_tile = [&](int buf) {
-        bf16 *kd = k_lds + buf * KBUF + lrow * KST + 8 * lchunk;
-        bf16 *vd = v_lds + buf * VBUF + lrow * VST + 8 * lchunk;
+
+    // LDS read offsets (bytes within a stage); mt adds 32 rows, qs adds 16 rows
+    int koff[8];
 #pragma unroll
-        for (int ps = 0; ps < 4; ++ps) {
-            *reinterpret_cast<uint4 *>(kd + 16 * ps * KST) = kbuf[ps];
-            *reinterpret_cast<uint4 *>(vd + 16 * ps * VST) = vbuf[ps];
-        }
-    };
+    for (int ks = 0; ks < 8; ++ks)
+        koff[ks] = col * ROWB + 16 * ((2 * ks + hl) ^ swz(col & 15));
+    // V^T read pattern: 16-lane group g = lane/16 covers head-dim half (g & 1) and
+    // key quarter (g >> 1); lane i of the group reads key row (i >> 2), dims 4*(i & 3)
+    const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    int voff0[4], voff1[4];
+#pragma unroll
+    for (int mtd = 0; mtd < 4; ++mtd) {
+        voff0[mtd] = TILEB + tr_row * ROWB + 16 * ((4 * mtd + tr_chunk) ^ swz(tr_row)) + 8 * (lane & 1);
+        voff1[mtd] = TILEB + (tr_row + 8) * ROWB + 16 * ((4 * mtd + tr_chunk) ^ swz(tr_row + 8)) + 8 * (lane & 1);
+    }
 
     f32x16 acc_o[4];
 #pragma unroll
@@ -169,31 +194,40 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const float sl2 = a.scale_log2;
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-    // V^T read pattern: 16-lane group g = lane/16 covers head-dim half (g & 1) and
-    // key quarter (g >> 1); lane i of the group points at key row (i >> 2), dims 4*(i & 3)
-    const int tr_row = 4 * (lane >> 5) + ((lane & 15) >> 2);
-    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-    load_tile(0);
-    store_tile(0);
+    int32_t tbl[4] = {0, 0, 0, 0};
+    load_tbl(0, tbl);
+    issue_tile(stage0, 0, tbl);
     if (n_kt > 1)
-        load_tile(1);
+        load_tbl(1, tbl);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
     __syncthreads();
 
-    for (int kt = 0; kt < n_kt; ++kt) {
-        const int cur = kt & 1;
-        const bf16 *kl = k_lds + cur * KBUF;
-        const bf16 *vl = v_lds + cur * VBUF;
+    // one tile: compute tile kt from stage ST while tile kt+1 streams into the other stage
+    auto step = [&](auto st_c, int kt) {
+        constexpr int ST = decltype(st_c)::value;
+        const char *cur = ST == 0 ? stage0 : stage1;
+        char *nxt = ST == 0 ? stage1 : stage0;
+        if (kt + 1 < n_kt) {
+            issue_tile(nxt, kt + 1, tbl);
+            if (kt + 2 < n_kt)
+                load_tbl(kt + 2, tbl);
+        }
 
+        bf16x8 kf[2][8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+                kf[mt][ks] = *reinterpret_cast<const bf16x8 *>(cur + koff[ks] + 32 * ROWB * mt);
         f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(kl + (32 * mt + col) * KST + 16 * ks + 8 * hl);
-                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[ks], sacc[mt], 0, 0, 0);
-            }
-        }
+            for (int mt = 0; mt < 2; ++mt)
+                sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][ks], qreg[ks], sacc[mt], 0, 0, 0);
+        // all 16 K reads are issued before the first MFMA, so their latencies overlap
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 
         const int kbase = kt * BN;
         if (kbase + BN - 1 > wave_min_kmax) {
@@ -211,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, sacc[mt][v]);
-        tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+        tmax = fmaxf(tmax, other_half(tmax, hl));
         const float mcand = tmax * sl2;
         const bool grow = mcand > m + kLazyTau;
         if (__builtin_amdgcn_ballot_w64(grow)) {   // wave-uniform: rescale only when a max grew
@@ -239,23 +273,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
 
 #pragma unroll
         for (int qs = 0; qs < 4; ++qs) {
-            const bf16 *vrow = vl + (16 * qs + tr_row) * VST + tr_col;
 #pragma unroll
             for (int mtd = 0; mtd < 4; ++mtd) {
-                const bf16x8 va = read_vt(vrow + 32 * mtd, vrow + 8 * VST + 32 * mtd);
+                const bf16x8 va = read_vt(cur + voff0[mtd] + 16 * ROWB * qs, cur + voff1[mtd] + 16 * ROWB * qs);
                 acc_o[mtd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qs], acc_o[mtd], 0, 0, 0);
             }
         }
 
-        if (kt + 1 < n_kt) {
-            store_tile(cur ^ 1);
-            if (kt + 2 < n_kt)
-                load_tile(kt + 2);
-        }
-        __syncthreads();
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile kt+1 has landed (this wave's part)
+        __syncthreads();                      // ... and every wave's part; stage ST is free again
+    };
+
+    for (int kt = 0; kt < n_kt; kt += 2) {
+        step(std::integral_constant<int, 0>{}, kt);
+        if (kt + 1 < n_kt)
+            step(std::integral_constant<int, 1>{}, kt + 1);
     }
 
-    l += shfl_xor_f(l, 32);
+    l += other_half(l, hl);
     if (col_valid) {
         const float inv = 1.f / l;
         uint16_t *op = static_cast<uint16_t *>(a.out) + ((int64_t)(q0 + qrow) * Hq + head) * D;
@@ -272,18 +307,186 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     }
 }
 
+// One workgroup per work item; items in the order (qb descending, s, kvh), so
+// the heaviest query blocks are dispatched first and blockIdx mod Hkv = kvh.
+template <int G, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
+{
+    constexpr int BM = 128 / G;
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGEB];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGEB];
+    const int Hkv = a.num_kv_heads, S = a.num_seqs;
+    const int n_qblk = (a.max_seqlen_q + BM - 1) / BM;
+    int idx = blockIdx.x;
+    const int kvh = idx % Hkv;
+    idx /= Hkv;
+    const int s = idx % S;
+    const int qb = n_qblk - 1 - idx / S;
+    if (qb * BM >= a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s])
+        return;
+    attend_block<G, MODE>(a, s, qb, kvh, stage0, stage1);
+}
+
+constexpr int kMaxLevels = 1024;   // query-block levels the persistent schedule supports
+
+// Persistent form: a grid of P workgroups (a multiple of 8, about two per CU)
+// walks the non-empty items in the same heavy-first order.  Level L holds the
+// query blocks qb = L of every sequence with more than L blocks, L from the top
+// down; within a level items go by sequence, then KV head.  The items whose rank
+// is x mod 8 belong to the P/8 workgroups with blockIdx mod 8 = x (the
+// dispatcher places those on one XCD, and for Hkv dividing 8 they share the KV
+// head), dealt in a snake order: in round k the j-th workgroup of the class
+// takes position k*P/8 + j when k is even and k*P/8 + P/8-1-j when k is odd,
+// which balances the decreasing item costs.  Every workgroup derives the same
+// schedule from cu_seqlens_q, so no state is shared between workgroups or calls.
+template <int G, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void prefill_persistent_kernel(PrefillArgs a)
+{
+    constexpr int BM = 128 / G;
+    __shared__ __attribute__((aligned(1024))) char stage0[STAGEB];
+    __shared__ __attribute__((aligned(1024))) char stage1[STAGEB];
+    __shared__ int lvl_cnt[kMaxLevels];     // sequences with more than L query blocks
+    __shared__ int lvl_start[kMaxLevels];   // rank of the first item of level L
+    const int Hkv = a.num_kv_heads, S = a.num_seqs;
+    const int n_lvl = (a.max_seqlen_q + BM - 1) / BM;   // <= kMaxLevels (checked by the host)
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+
+    auto n_blocks = [&](int q) {
+        const int len = a.cu_seqlens_q[q + 1] - a.cu_seqlens_q[q];
+        return min((len + BM - 1) / BM, n_lvl);
+    };
+    // histogram of per-sequence query-block counts: lvl_cnt[i] = #{s : blocks(s) = i + 1}
+    for (int i = tid; i < n_lvl; i += kThreads)
+        lvl_cnt[i] = 0;
+    __syncthreads();
+    for (int q = tid; q < S; q += kThreads) {
+        const int nb = n_blocks(q);
+        if (nb > 0)
+            atomicAdd(&lvl_cnt[nb - 1], 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // suffix sums over levels, lane i owning levels [i*C, i*C + C)
+        const int C = (n_lvl + kWave - 1) / kWave;   // <= 16
+        int cnt[16];
+        int local = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            const int L = lane * C + c;
+            cnt[c] = (c < C && L < n_lvl) ? lvl_cnt[L] : 0;
+            local += cnt[c];
+        }
+        int suf = local;                             // inclusive suffix over lanes
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_down(suf, d, kWave);
+            if (lane + d < kWave) suf += v;
+        }
+        int run = suf - local;                       // levels above this lane's chunk
+#pragma unroll
+        for (int c = 15; c >= 0; --c) {
+            run += cnt[c];                           // cnt[c] is 0 outside the chunk
+            cnt[c] = (c < C && lane * C + c < n_lvl) ? run : 0;   // sequences with more than L blocks
+        }
+        int local2 = 0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) local2 += cnt[c];
+        int suf2 = local2;
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int v = __shfl_down(suf2, d, kWave);
+            if (lane + d < kWave) suf2 += v;
+        }
+        int run2 = suf2 - local2;
+#pragma unroll
+        for (int c = 15; c >= 0; --c) {
+            const int L = lane * C + c;
+            if (c < C && L < n_lvl) {
+                lvl_cnt[L] = cnt[c];
+                lvl_start[L] = run2 * Hkv;
+            }
+            run2 += cnt[c];
+        }
+    }
+    __syncthreads();
+    const int total = (lvl_start[0] + lvl_cnt[0] * Hkv);   // non-empty items
+
+    const int P8 = gridDim.x / 8, x = blockIdx.x % 8, j = blockIdx.x / 8;
+    for (int k = 0;; ++k) {
+        const int pos = k * P8 + ((k & 1) ? P8 - 1 - j : j);
+        const int rank = 8 * pos + x;
+        if (rank >= total)
+            break;
+        // level: the smallest L with lvl_start[L] <= rank
+        int lo = 0, hi = n_lvl - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (lvl_start[mid] <= rank) hi = mid; else lo = mid + 1;
+        }
+        const int L = lo;
+        const int within = rank - lvl_start[L];
+        const int kvh = within % Hkv;
+        int t = within / Hkv;                        // the t-th sequence with more than L blocks
+        int s = -1;
+        for (int base = 0; base < S; base += kWave) {
+            const int q = base + lane;
+            const bool f = q < S && n_blocks(q) > L;
+            const uint64_t b = __builtin_amdgcn_ballot_w64(f);
+            const int c = __builtin_popcountll(b);
+            if (t < c) {
+                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+                const uint64_t me = __builtin_amdgcn_ballot_w64(f && below == t);
+                s = base + __builtin_ctzll(me);
+                break;
+            }
+            t -= c;
+        }
+        if (s < 0)   // cannot happen: the counts and the scan use the same block counts
+            break;
+        attend_block<G, MODE>(a, s, L, kvh, stage0, stage1);
+    }
+}
+
+int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int G>
 hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
 {
     constexpr int BM = 128 / G;
     const int64_t n_qblk = (a.max_seqlen_q + BM - 1) / BM;
-    const dim3 grid((uint32_t)(n_qblk * a.num_seqs * a.num_kv_heads));
-    if (!a.paged)
-        hipLaunchKernelGGL((prefill_kernel<G, kFlat>), grid, dim3(kThreads), 0, stream, a);
-    else if (a.block_size % BN == 0)
-        hipLaunchKernelGGL((prefill_kernel<G, kPagedTile>), grid, dim3(kThreads), 0, stream, a);
-    else
-        hipLaunchKernelGGL((prefill_kernel<G, kPagedRow>), grid, dim3(kThreads), 0, stream, a);
+    const int64_t items = n_qblk * a.num_seqs * a.num_kv_heads;
+    const int64_t slots = 2 * (int64_t)device_cus();
+    const int mode = !a.paged ? kFlat : (a.block_size % BN == 0 ? kPagedTile : kPagedRow);
+    if (items > slots && n_qblk <= kMaxLevels) {
+        const dim3 grid((uint32_t)((slots + 7) / 8 * 8));
+        if (mode == kFlat)
+            hipLaunchKernelGGL((prefill_persistent_kernel<G, kFlat>), grid, dim3(kThreads), 0, stream, a);
+        else if (mode == kPagedTile)
+            hipLaunchKernelGGL((prefill_persistent_kernel<G, kPagedTile>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_persistent_kernel<G, kPagedRow>), grid, dim3(kThreads), 0, stream, a);
+    } else {
+        const dim3 grid((uint32_t)items);
+        if (mode == kFlat)
+            hipLaunchKernelGGL((prefill_kernel<G, kFlat>), grid, dim3(kThreads), 0, stream, a);
+        else if (mode == kPagedTile)
+            hipLaunchKernelGGL((prefill_kernel<G, kPagedTile>), grid, dim3(kThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((prefill_kernel<G, kPagedRow>), grid, dim3(kThreads), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

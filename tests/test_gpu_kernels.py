@@ -180,6 +180,26 @@ def test_prefill_empty_sequences(pa, orc):
     _check(pa, orc, wl, "empty chunks")
 
 
+@pytest.mark.parametrize("hq,hkv,bs,paged", [(16, 8, 256, True), (8, 1, 16, True),
+                                             (8, 8, 64, False), (32, 8, 64, True)],
+                         ids=["g2-tile", "g8-row", "g1-flat", "g4-tile"])
+def test_prefill_many_query_blocks(pa, orc, hq, hkv, bs, paged):
+    """Batches with more query blocks than the chip has workgroup slots (2 per
+    CU) take the persistent schedule: every (query block, sequence, KV head)
+    item must be computed exactly once, whatever the mix of lengths (empty
+    chunks, single rows, tile and block edges, long tails)."""
+    rng = np.random.default_rng(18 + hq + hkv)
+    q = [0, 1, 15, 63, 64, 65, 200, 700, 0, 129] + rng.integers(1, 600, size=30).tolist()
+    pre = rng.integers(0, 300, size=len(q)) if paged else np.zeros(len(q), np.int64)
+    k = (np.array(q) + pre).tolist()
+    wl = _wl(q_lens=q, k_lens=k, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
+             paged=paged, seed=19)
+    g = hq // hkv
+    items = -(-max(q) // (128 // g)) * len(q) * hkv
+    assert items > 2 * 256, "the batch must exceed one workgroup per slot"
+    _check(pa, orc, wl, f"many blocks Hq={hq} Hkv={hkv} bs={bs} paged={paged}")
+
+
 # ------------------------------------------------------------------ decode
 
 CTX = [1, 2, 31, 32, 255, 256, 257, 511, 512, 513, 1000, 2049]
