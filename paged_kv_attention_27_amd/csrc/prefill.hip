@@ -131,7 +131,10 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
     const int lpos = lane & 15;
     const int n_blk = MODE == kFlat ? 0 : (k_len + bs - 1) / bs;
 
-    auto block_of = [&](int key) { return shift >= 0 ? (key >> shift) : (key / bs); };
+    // per-tile paging needs a power-of-two block size (launch condition), so a shift
+    auto block_of = [&](int key) {
+        return MODE == kPagedTile ? (key >> shift) : (shift >= 0 ? (key >> shift) : (key / bs));
+    };
     // block-table entries the copy of tile t needs, read into registers one tile ahead
     auto load_tbl = [&](int t, int32_t (&tbl)[4]) {
         if (MODE == kPagedTile) {
@@ -144,30 +147,43 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
                 tbl[j] = bt_row[block_of(min(t * BN + 16 * wave + 4 * j + lsub, k_len - 1))];
         }
     };
+    // byte offset, from the tile's first row, of the 16 bytes lane copies in instruction j
+    const uint32_t row_bytes = (uint32_t)row_elems * 2;
+    uint32_t coff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        coff[j] = (uint32_t)(16 * wave + 4 * j + lsub) * row_bytes + kvh * ROWB + 16 * (lpos ^ (4 * lsub + j));
     auto issue_tile = [&](char *stage, int t, const int32_t (&tbl)[4]) {
         const int key0 = t * BN;
         const int last = k_len - 1 - key0;   // rows past it copy this row
-        int64_t tile_row0 = 0;
+        if (MODE == kPagedRow) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int key = key0 + min(16 * wave + 4 * j + lsub, last);
+                const int64_t row = (int64_t)tbl[j] * bs + (key - block_of(key) * bs);
+                const int64_t e = row * row_elems + kvh * D + 8 * (lpos ^ (4 * lsub + j));
+                char *dst = stage + (16 * wave + 4 * j) * ROWB;
+                __builtin_amdgcn_global_load_lds((global_void *)(ksrc + e), (lds_void *)dst, 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((global_void *)(vsrc + e), (lds_void *)(dst + TILEB), 16, 0, 0);
+            }
+            return;
+        }
+        // the tile's rows are consecutive pool rows: one scalar base plus 32-bit lane offsets
+        int64_t tile_row0;
         if (MODE == kFlat) {
             tile_row0 = (int64_t)k0 + key0;
-        } else if (MODE == kPagedTile) {
+        } else {
             const int lb = block_of(key0);
             tile_row0 = (int64_t)__builtin_amdgcn_readfirstlane(tbl[0]) * bs + (key0 - lb * bs);
         }
+        const char *kb = reinterpret_cast<const char *>(ksrc) + tile_row0 * row_bytes;
+        const char *vb = reinterpret_cast<const char *>(vsrc) + tile_row0 * row_bytes;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int r = min(16 * wave + 4 * j + lsub, last);
-            int64_t row;
-            if (MODE == kPagedRow) {
-                const int key = key0 + r;
-                row = (int64_t)tbl[j] * bs + (key - block_of(key) * bs);
-            } else {
-                row = tile_row0 + r;
-            }
-            const int64_t e = row * row_elems + kvh * D + 8 * (lpos ^ (4 * lsub + j));
+            const uint32_t o = coff[j] - (uint32_t)max(16 * wave + 4 * j + lsub - last, 0) * row_bytes;
             char *dst = stage + (16 * wave + 4 * j) * ROWB;
-            __builtin_amdgcn_global_load_lds((global_void *)(ksrc + e), (lds_void *)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((global_void *)(vsrc + e), (lds_void *)(dst + TILEB), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((global_void *)(kb + o), (lds_void *)dst, 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((global_void *)(vb + o), (lds_void *)(dst + TILEB), 16, 0, 0);
         }
     };
 
@@ -207,11 +223,10 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         constexpr int ST = decltype(st_c)::value;
         const char *cur = ST == 0 ? stage0 : stage1;
         char *nxt = ST == 0 ? stage1 : stage0;
-        if (kt + 1 < n_kt) {
-            issue_tile(nxt, kt + 1, tbl);
-            if (kt + 2 < n_kt)
-                load_tbl(kt + 2, tbl);
-        }
+        // copy of the next tile (the last tile re-copies itself into the stage no step reads
+        // again, which keeps this part branch-free so the copies interleave with the MFMAs)
+        issue_tile(nxt, min(kt + 1, n_kt - 1), tbl);
+        load_tbl(min(kt + 2, n_kt - 1), tbl);
 
         bf16x8 kf[2][8];
 #pragma unroll
@@ -225,9 +240,15 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][ks], qreg[ks], sacc[mt], 0, 0, 0);
-        // all 16 K reads are issued before the first MFMA, so their latencies overlap
+        // all 16 K reads are issued before the first MFMA, so their latencies overlap; the
+        // next tile's copies are spread between the MFMAs so their issue never stalls the wave
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
 
         const int kbase = kt * BN;
         if (kbase + BN - 1 > wave_min_kmax) {
@@ -469,7 +490,8 @@ hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
     const int64_t n_qblk = (a.max_seqlen_q + BM - 1) / BM;
     const int64_t items = n_qblk * a.num_seqs * a.num_kv_heads;
     const int64_t slots = 2 * (int64_t)device_cus();
-    const int mode = !a.paged ? kFlat : (a.block_size % BN == 0 ? kPagedTile : kPagedRow);
+    const bool pow2 = (a.block_size & (a.block_size - 1)) == 0;
+    const int mode = !a.paged ? kFlat : (a.block_size % BN == 0 && pow2 ? kPagedTile : kPagedRow);
     if (items > slots && n_qblk <= kMaxLevels) {
         const dim3 grid((uint32_t)((slots + 7) / 8 * 8));
         if (mode == kFlat)
