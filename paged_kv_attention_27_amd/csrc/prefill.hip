@@ -73,6 +73,16 @@ __device__ __forceinline__ bf16x8 read_vt(const char *p0, const char *p1) {
     return __builtin_bit_cast(bf16x8, ab);
 }
 
+// 16 bytes per lane from base + off into the LDS span at dst (lane i -> dst + 16 i).
+// The buffer form (a descriptor built from the wave-uniform base) keeps the
+// copy a pure vector-memory operation, so waits on LDS reads stay exact.
+__device__ __forceinline__ void copy16_to_lds(const char *base, uint32_t off, char *dst)
+{
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), 0, 0x7fffffff, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, 0);
+}
+
 // value of x held by lane (lane xor 32)
 __device__ __forceinline__ float other_half(float x, int hl) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -182,8 +192,8 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         for (int j = 0; j < 4; ++j) {
             const uint32_t o = coff[j] - (uint32_t)max(16 * wave + 4 * j + lsub - last, 0) * row_bytes;
             char *dst = stage + (16 * wave + 4 * j) * ROWB;
-            __builtin_amdgcn_global_load_lds((global_void *)(kb + o), (lds_void *)dst, 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((global_void *)(vb + o), (lds_void *)(dst + TILEB), 16, 0, 0);
+            copy16_to_lds(kb, o, dst);
+            copy16_to_lds(vb, o, dst + TILEB);
         }
     };
 
