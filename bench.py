@@ -339,7 +339,7 @@ def main():
             prefill[pwl.name] = {
                 "value": round(tflops, 2), "unit": "TFLOP/s", "flops": ps.flops,
                 "ms_attention": round(float(t_attn), 5), "ms_store": round(float(t_store), 5),
-                "roofline": {"kernel": "prefill_kernel", "bound": "mfma",
+                "roofline": {"kernel": "prefill_persistent_kernel", "bound": "mfma",
                              "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                              "traffic": traffic_for(f"prefill_{pwl.name}", PREFILL_SRC)}}
