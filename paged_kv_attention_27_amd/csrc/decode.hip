@@ -105,6 +105,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     const int n_chunks = (t_stop - t_begin + kChunk - 1) / kChunk;
     const int64_t lane_off = (int64_t)(r * U) * row_elems + kvh * D + 8 * c;
 
+    // every K/V byte is read once: nontemporal loads (measured on MI355X: a plain
+    // 2 GiB streaming read goes from ~6.1 to ~7.0 TB/s with the hint)
+    auto ld = [](const bf16 *p) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+        return make_uint4(v[0], v[1], v[2], v[3]);
+    };
     for (int ch = wave; ch < n_chunks; ch += kWaves) {
         const int cs = t_begin + ch * kChunk;
         const int base = cs + r * U;
@@ -118,8 +124,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const bool ok = base + u < t_stop;
-                kr[u] = ok ? *reinterpret_cast<const uint4 *>(kb + u * row_elems) : make_uint4(0, 0, 0, 0);
-                vr[u] = ok ? *reinterpret_cast<const uint4 *>(vb + u * row_elems) : make_uint4(0, 0, 0, 0);
+                kr[u] = ok ? ld(kb + u * row_elems) : make_uint4(0, 0, 0, 0);
+                vr[u] = ok ? ld(vb + u * row_elems) : make_uint4(0, 0, 0, 0);
             }
         } else {
 #pragma unroll
@@ -128,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
                 if (j < t_stop) {
                     const int lb = shift >= 0 ? (j >> shift) : (j / bs);
                     const int64_t off = ((int64_t)bt_row[lb] * bs + (j - lb * bs)) * row_elems + kvh * D + 8 * c;
-                    kr[u] = *reinterpret_cast<const uint4 *>(kc + off);
-                    vr[u] = *reinterpret_cast<const uint4 *>(vc + off);
+                    kr[u] = ld(kc + off);
+                    vr[u] = ld(vc + off);
                 } else {
                     kr[u] = make_uint4(0, 0, 0, 0);
                     vr[u] = make_uint4(0, 0, 0, 0);
