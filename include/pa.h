@@ -37,8 +37,9 @@
  *   Device-resident values (slots, tables, lengths) are not validated: values
  *   outside the ranges stated below are undefined behaviour.  A failed launch
  *   returns PA_ERR_LAUNCH.
- * Threads.  No global state: entry points are re-entrant; calls on one stream
- *   execute in order.
+ * Threads.  The device entry points keep no state between calls (only each
+ *   device's compute-unit count, read once) and are re-entrant; calls on one
+ *   stream execute in order.  A block manager (pa_bm_*) belongs to one thread.
  */
 #ifndef PA_H
 #define PA_H

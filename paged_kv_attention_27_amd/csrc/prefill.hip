@@ -42,6 +42,7 @@
 // XCD so its K/V stays in that L2.
 #include "pa_common.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace pa {
@@ -478,19 +479,21 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_persistent_kernel(Prefill
     }
 }
 
+// compute units of the current device (queried once per device; concurrent
+// first calls store the same value)
 int device_cus()
 {
-    static int cus[64] = {0};
+    static std::atomic<int> cus[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
         return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
-        cus[dev] = n;
+        cus[dev].store(n, std::memory_order_relaxed);
     }
-    return cus[dev];
+    return n;
 }
 
 template <int G>
