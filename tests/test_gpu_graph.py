@@ -130,3 +130,66 @@ def test_decode_graph_buckets(orc):
         check_close(got, ref, f"bucket step {step} (S={S})")
     torch.cuda.synchronize()
     assert np.array_equal(host_u16(kc), ok) and np.array_equal(host_u16(vc), ov)
+
+
+def test_prefill_graph_replays(orc):
+    """The chunked prefill (store of the new tokens, then attention over the pools)
+    captured once and replayed with new values: batches with more query blocks
+    than two per CU take the persistent schedule, which must keep no state
+    between launches."""
+    import paged_kv_attention_27_amd as pa
+    from paged_kv_attention_27_amd import workloads
+    q_lens = [700, 64, 1, 300, 129, 512, 33, 1000, 90, 257, 640, 5]
+    k_lens = [q + p for q, p in zip(q_lens, [0, 512, 40, 100, 0, 256, 7, 24, 300, 0, 64, 500])]
+    wl = workloads.synthetic(q_lens=q_lens, k_lens=k_lens, block_size=256, seed=41)
+    items = -(-max(q_lens) // 64) * len(q_lens) * wl.num_kv_heads
+    assert items > 512, "the batch must take the persistent schedule"
+    kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
+    ok, ov = wl.k_cache.copy(), wl.v_cache.copy()
+    ph, fx = wl.prefill, wl.prefix
+    pa.pa_store_kv(dev_bf16(fx.k), dev_bf16(fx.v), kc, vc,
+                   pa.pa_slot_mapping(fx.cu_seqlens_q, fx.seqlens_k, prefix_tables(wl), 256).cuda())
+    orc.store(fx.k, fx.v, orc.slot_mapping(fx.cu_seqlens_q, fx.seqlens_k, prefix_tables(wl), 256),
+              ok, ov)
+    slots = pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, 256).cuda()
+    cu_q = dev_i32(ph.cu_seqlens_q)
+    cu_k = dev_i32(np.concatenate([[0], np.cumsum(ph.seqlens_k)]).astype(np.int32))
+    bt = dev_i32(wl.block_tables)
+    q_s = torch.empty((int(ph.cu_seqlens_q[-1]), wl.num_q_heads, 128), dtype=torch.bfloat16,
+                      device="cuda")
+    k_s = torch.empty((int(ph.cu_seqlens_q[-1]), wl.num_kv_heads, 128), dtype=torch.bfloat16,
+                      device="cuda")
+    v_s = torch.empty_like(k_s)
+    out_s = torch.empty_like(q_s)
+    k_s.zero_(), v_s.zero_(), q_s.zero_()
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            pa.pa_store_kv(k_s, v_s, kc, vc, slots, stream=stream)
+            pa.pa_prefill_varlen(q_s, None, None, kc, vc, bt, cu_q, cu_k, ph.max_seqlen_q,
+                                 ph.max_seqlen_k, wl.num_kv_heads, wl.scale, out=out_s,
+                                 stream=stream)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(42)
+    for r in range(3):
+        q = workloads.normal_bf16(rng, tuple(q_s.shape), 2.0 if r == 1 else 1.0)
+        k = workloads.normal_bf16(rng, tuple(k_s.shape))
+        v = workloads.normal_bf16(rng, tuple(v_s.shape))
+        q_s.copy_(dev_bf16(q)), k_s.copy_(dev_bf16(k)), v_s.copy_(dev_bf16(v))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = host_f64(out_s)
+        eager = pa.pa_prefill_varlen(dev_bf16(q), None, None, kc, vc, bt, cu_q, cu_k,
+                                     ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale)
+        torch.cuda.synchronize()
+        orc.store(k, v, orc.slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, 256),
+                  ok, ov)
+        ref = orc.attention(q, ph.cu_seqlens_q, k_cache=ok, v_cache=ov,
+                            block_tables=wl.block_tables, seqlens_k=ph.seqlens_k, scale=wl.scale)
+        log(f"prefill replay {r}")
+        check_close(got, ref, f"prefill graph replay {r}")
+        assert np.array_equal(host_u16(out_s), host_u16(eager)), "replay differs from eager call"
+    assert np.array_equal(host_u16(kc), ok) and np.array_equal(host_u16(vc), ov)
