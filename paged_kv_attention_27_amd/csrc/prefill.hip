@@ -27,19 +27,22 @@
 // more than 2^8, so weights stay <= 256 and most tiles skip the rescale.
 //
 // K/V tiles of 64 keys go from global memory straight into LDS
-// (global_load_lds_dwordx4: lane i of an instruction fills the i-th 16-byte
-// chunk of a 1 KB span, i.e. 4 tile rows), double-buffered in two LDS stages:
-// the copy of tile t+1 is issued before tile t is computed and waited for at
-// the end of the step, so it overlaps a whole tile of work and costs no
-// registers.  Rows are 256 B with no padding; the 16-byte chunk c of row r is
+// (buffer_load_dwordx4 ... lds, or global_load_lds_dwordx4 for per-row paging:
+// lane i of an instruction fills the i-th 16-byte chunk of a 1 KB span, i.e. 4
+// tile rows), double-buffered in two LDS stages: the copy of tile t+1 is
+// issued between the S MFMAs of tile t and waited for at the end of the step,
+// so it overlaps a whole tile of work and costs no registers.  Batches with
+// more query blocks than two per CU run a persistent grid with a heavy-first
+// schedule every workgroup derives from cu_seqlens_q (see
+// prefill_persistent_kernel).  Rows are 256 B with no padding; the 16-byte chunk c of row r is
 // stored at position c ^ swz(r mod 16), swz(r) = 4 (r mod 4) + (r div 4) mod 4,
 // which keeps both the b128 K reads (16 rows, one chunk) and the transposing V
 // reads (4 rows, 2-4 chunks) free of bank conflicts.  Rows past k_len load a
 // copy of the last valid row, so every V value is finite and every key past
 // k_len is removed by the causal mask.  The block tables are read one tile
-// ahead with vector loads.  Heaviest query blocks are dispatched first;
-// blockIdx mod Hkv = KV head keeps every block of a (sequence, KV head) on one
-// XCD so its K/V stays in that L2.
+// ahead with vector loads.  Heaviest query blocks go first; workgroups whose
+// blockIdx agree mod 8 (one XCD) share a KV head when Hkv divides 8, so its K/V
+// stays in that L2.
 #include "pa_common.h"
 
 #include <atomic>
