@@ -197,6 +197,12 @@ class PrefillSetup:
         self.cu_k = dev_i32(torch, cu_k)
         self.out = torch.empty_like(self.q)
         self.flops = prefill_flops(wl, ph)
+        # the workspace lets batches with few query blocks per CU split long blocks
+        n_seqs = len(ph.cu_seqlens_q) - 1
+        self.ws = pa.pa_prefill_workspace(n_seqs, ph.max_seqlen_q, ph.max_seqlen_k,
+                                          wl.num_q_heads, wl.num_kv_heads)
+        self.split = pa.pa_prefill_workspace_size(n_seqs, ph.max_seqlen_q, ph.max_seqlen_k,
+                                                  wl.num_q_heads, wl.num_kv_heads) > 0
         torch.cuda.synchronize()
 
     def attention(self):
@@ -204,11 +210,11 @@ class PrefillSetup:
         if ph.paged:
             pa.pa_prefill_varlen(self.q, None, None, self.kc, self.vc, self.bt, self.cu_q, self.cu_k,
                                  ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale,
-                                 out=self.out, stream=self.stream)
+                                 out=self.out, stream=self.stream, workspace=self.ws)
         else:
             pa.pa_prefill_varlen(self.q, self.k, self.v, None, None, None, self.cu_q, self.cu_k,
                                  ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale,
-                                 out=self.out, stream=self.stream)
+                                 out=self.out, stream=self.stream, workspace=self.ws)
 
     def time(self, steps, warmup):
         torch, pa = self.torch, self.pa
@@ -339,12 +345,13 @@ def main():
             prefill[pwl.name] = {
                 "value": round(tflops, 2), "unit": "TFLOP/s", "flops": ps.flops,
                 "ms_attention": round(float(t_attn), 5), "ms_store": round(float(t_store), 5),
+                "key_split": ps.split,
                 "roofline": {"kernel": "prefill_persistent_kernel", "bound": "mfma",
                              "achieved": round(tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                              "traffic": traffic_for(f"prefill_{pwl.name}", PREFILL_SRC)}}
             log(f"prefill {pwl.name}: attention {t_attn * 1e3:.1f} us = {tflops:.1f} TFLOP/s, "
-                f"store {t_store * 1e3:.1f} us")
+                f"store {t_store * 1e3:.1f} us{' (key split)' if ps.split else ''}")
             del ps
         result["prefill"] = prefill
         lwl = workloads.make(5)

@@ -145,6 +145,43 @@ int pa_prefill_varlen(const void *q, const void *k, const void *v,
                       int32_t block_size, float scale, void *out, hipStream_t stream);
 
 /*
+ * Bytes of device workspace pa_prefill_varlen_ws needs for these sizes on the
+ * current device; 0 when such a batch is not split (then the workspace is
+ * ignored and may be NULL) or the sizes are invalid.  A batch is split when it
+ * has at most one (query block, sequence, KV head) item per two compute units
+ * and max_seqlen_k >= 2048: few, long items, whose length then sets the time.
+ */
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * pa_prefill_varlen with a workspace: the same operation and arguments, plus
+ * a key split for batches of few, long query blocks (see
+ * pa_prefill_workspace_size; there the longest blocks set the time).  Each query block with at least 4 key tiles of
+ * 64 keys is then computed as two halves of its key range by two workgroups;
+ * the second to finish merges the two partial softmax states, rescaling both
+ * to the larger running maximum (the log-sum-exp combination that lets the
+ * blocked computation of [Atlas] ch.22 avoid the full score matrix).  Results
+ * differ from pa_prefill_varlen only by rounding (the partials are stored as
+ * fp16 O / l with fp32 max and sum).
+ *
+ * workspace  (device) >= pa_prefill_workspace_size(...) bytes, 16-byte aligned,
+ *            zero-filled before its first use; every call leaves it zero-filled
+ *            again (its arrival counters), so it can be reused without clearing.
+ *            Calls that share a workspace must not overlap in time (one stream).
+ * Errors as pa_prefill_varlen, plus PA_ERR_WORKSPACE (workspace_bytes too small)
+ * and PA_ERR_NULL (workspace NULL while one is needed).
+ */
+int pa_prefill_varlen_ws(const void *q, const void *k, const void *v,
+                         const void *k_cache, const void *v_cache,
+                         const int32_t *block_tables, int32_t max_blocks_per_seq,
+                         const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                         int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, float scale, void *workspace,
+                         size_t workspace_bytes, void *out, hipStream_t stream);
+
+/*
  * Number of key partitions pa_decode splits the longest context into, for
  * the given partition_size (0 = the library's choice for these sizes).
  * Returns 0 for invalid sizes.

@@ -50,6 +50,11 @@ def load():
     lib.pa_prefill_varlen.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                       _I, _I, ctypes.c_float, _P, _P]
+    lib.pa_prefill_varlen_ws.restype = ctypes.c_int
+    lib.pa_prefill_varlen_ws.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                         _I, _I, ctypes.c_float, _P, _SZ, _P, _P]
+    lib.pa_prefill_workspace_size.restype = ctypes.c_size_t
+    lib.pa_prefill_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.pa_decode_num_partitions.restype = ctypes.c_int32
     lib.pa_decode_num_partitions.argtypes = [_I, _I, _I, _I]
     lib.pa_decode_workspace_size.restype = ctypes.c_size_t
@@ -136,9 +141,25 @@ def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
     _check("pa_store_kv", st)
 
 
+def pa_prefill_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads,
+                              head_dim=128):
+    return int(load().pa_prefill_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                                num_kv_heads, head_dim))
+
+
+def pa_prefill_workspace(num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads,
+                         head_dim=128):
+    """A zero-filled device workspace for pa_prefill_varlen(..., workspace=...)."""
+    need = pa_prefill_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                     num_kv_heads, head_dim)
+    return torch.zeros(max(need, 16), dtype=torch.uint8, device="cuda")
+
+
 def pa_prefill_varlen(q, k, v, k_cache, v_cache, block_tables, cu_seqlens_q, cu_seqlens_k,
                       max_seqlen_q, max_seqlen_k, num_kv_heads, scale, out=None,
-                      block_size=None, stream=None):
+                      block_size=None, stream=None, workspace=None):
+    """Varlen causal prefill (include/pa.h).  With a workspace (see pa_prefill_workspace)
+    the call goes through pa_prefill_varlen_ws, which may split long query blocks."""
     Tq, Hq, d = q.shape
     num_seqs = cu_seqlens_q.numel() - 1
     if out is None:
@@ -149,7 +170,7 @@ def pa_prefill_varlen(q, k, v, k_cache, v_cache, block_tables, cu_seqlens_q, cu_
         maxb = block_tables.shape[1]
     else:
         bs, maxb = (1 if block_size is None else block_size), 0
-    st = load().pa_prefill_varlen(
+    common = (
         _dev(q, torch.bfloat16, "q"),
         _dev(k, torch.bfloat16, "k", optional=True),
         _dev(v, torch.bfloat16, "v", optional=True),
@@ -159,8 +180,15 @@ def pa_prefill_varlen(q, k, v, k_cache, v_cache, block_tables, cu_seqlens_q, cu_
         _dev(cu_seqlens_q, torch.int32, "cu_seqlens_q"),
         _dev(cu_seqlens_k, torch.int32, "cu_seqlens_k"),
         num_seqs, int(max_seqlen_q), int(max_seqlen_k), Hq, int(num_kv_heads), d, int(bs),
-        float(scale), _dev(out, torch.bfloat16, "out"), _stream(stream))
-    _check("pa_prefill_varlen", st)
+        float(scale))
+    if workspace is None:
+        st = load().pa_prefill_varlen(*common, _dev(out, torch.bfloat16, "out"), _stream(stream))
+        _check("pa_prefill_varlen", st)
+    else:
+        st = load().pa_prefill_varlen_ws(*common, _dev(workspace, torch.uint8, "workspace"),
+                                         workspace.numel(), _dev(out, torch.bfloat16, "out"),
+                                         _stream(stream))
+        _check("pa_prefill_varlen_ws", st)
     return out
 
 

@@ -132,12 +132,28 @@ int pa_store_kv(const void *k, const void *v, void *k_cache, void *v_cache,
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
 }
 
-int pa_prefill_varlen(const void *q, const void *k, const void *v, const void *k_cache,
-                      const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
-                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
-                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
-                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
-                      void *out, hipStream_t stream)
+size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim)
+{
+    if (head_dim != kHeadDim || max_seqlen_k < max_seqlen_q)
+        return 0;
+    const int64_t items = pa::prefill_split_items(num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                                                  num_kv_heads);
+    if (items <= 0)
+        return 0;
+    // [items][2] partials, then [items] int32 arrival counters
+    return (size_t)items * 2 * pa::kPrefillPartBytes + (size_t)items * sizeof(int32_t);
+}
+
+namespace {
+
+int prefill_impl(const void *q, const void *k, const void *v, const void *k_cache,
+                 const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                 const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                 int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                 bool with_workspace, void *workspace, size_t workspace_bytes, void *out,
+                 hipStream_t stream)
 {
     const bool paged = block_tables != nullptr;
     if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_q_heads < 1 ||
@@ -177,14 +193,63 @@ int pa_prefill_varlen(const void *q, const void *k, const void *v, const void *k
     a.max_blocks = max_blocks_per_seq;
     a.num_seqs = num_seqs;
     a.max_seqlen_q = max_seqlen_q;
+    a.max_seqlen_k = max_seqlen_k;
     a.num_q_heads = num_q_heads;
     a.num_kv_heads = num_kv_heads;
     a.block_size = paged ? block_size : 1;
     a.bs_shift = log2_if_pow2(a.block_size);
     a.paged = paged;
     a.scale_log2 = scale * pa::kLog2e;
+    a.split = 0;
+    a.ws_part = nullptr;
+    a.ws_cnt = nullptr;
+    if (with_workspace) {
+        const size_t need = pa_prefill_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k,
+                                                      num_q_heads, num_kv_heads, head_dim);
+        if (need > 0) {
+            if (workspace_bytes < need)
+                return PA_ERR_WORKSPACE;
+            if (!workspace)
+                return PA_ERR_NULL;
+            if (!aligned16(workspace))
+                return PA_ERR_UNSUPPORTED;
+            const size_t items = (need / (2 * pa::kPrefillPartBytes + sizeof(int32_t)));
+            a.split = 1;
+            a.ws_part = workspace;
+            a.ws_cnt = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
+                                                   items * 2 * pa::kPrefillPartBytes);
+        }
+    }
     hipError_t e = pa::launch_prefill(a, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+int pa_prefill_varlen(const void *q, const void *k, const void *v, const void *k_cache,
+                      const void *v_cache, const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k, int32_t num_seqs,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, float scale,
+                      void *out, hipStream_t stream)
+{
+    return prefill_impl(q, k, v, k_cache, v_cache, block_tables, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                        num_kv_heads, head_dim, block_size, scale, false, nullptr, 0, out, stream);
+}
+
+int pa_prefill_varlen_ws(const void *q, const void *k, const void *v, const void *k_cache,
+                         const void *v_cache, const int32_t *block_tables,
+                         int32_t max_blocks_per_seq, const int32_t *cu_seqlens_q,
+                         const int32_t *cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_q,
+                         int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, float scale, void *workspace,
+                         size_t workspace_bytes, void *out, hipStream_t stream)
+{
+    return prefill_impl(q, k, v, k_cache, v_cache, block_tables, max_blocks_per_seq, cu_seqlens_q,
+                        cu_seqlens_k, num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads,
+                        num_kv_heads, head_dim, block_size, scale, true, workspace,
+                        workspace_bytes, out, stream);
 }
 
 int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

@@ -97,13 +97,28 @@ struct PrefillArgs {
     int32_t max_blocks;
     int32_t num_seqs;
     int32_t max_seqlen_q;
+    int32_t max_seqlen_k;
     int32_t num_q_heads;
     int32_t num_kv_heads;
     int32_t block_size;
     int32_t bs_shift;
     bool paged;
     float scale_log2;
+    // key-split mode (split != 0): an item with at least kPrefillMinSplitTiles key tiles
+    // is computed as two halves of its key range by two workgroups; each half stores
+    // its partial in ws_part and the second to arrive (counter ws_cnt) merges them
+    int32_t split;
+    void *ws_part;      // [items][2] partials of kPrefillPartBytes each
+    int32_t *ws_cnt;    // [items] arrival counters; zero between calls
 };
+// bytes of one half's partial: O / l as fp16 pairs [4 waves][32][64 lanes] u32, then the
+// column max and sum as fp32 [4 waves][2][64 lanes]
+constexpr size_t kPrefillPartBytes = (4 * 32 * 64 + 4 * 2 * 64) * 4;
+constexpr int kPrefillMinSplitTiles = 4;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+// items of a batch of these sizes that key-split mode would cover on the current
+// device (0: the batch is not split)
+int64_t prefill_split_items(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t num_q_heads, int32_t num_kv_heads);
 
 }  // namespace pa

@@ -95,11 +95,17 @@ __device__ __forceinline__ float other_half(float x, int hl) {
 
 // One work item: query block qb (BM = 128/g positions) of sequence s against KV
 // head kvh, through the two LDS stages.  The caller guarantees qb * BM < q_len.
-// Every path through it ends with a workgroup barrier, so items can follow each
-// other on the same stages.
+// Every path that touches the stages ends with a workgroup barrier, so items can
+// follow each other on the same stages.  half = -1: the whole key range, output
+// written here.  half = 0 / 1 (key-split mode): an item with at least
+// kPrefillMinSplitTiles key tiles is split at tile n/2; this call computes one half,
+// stores its partial (O / l in fp16, column max and sum in fp32), and the second of
+// the two workgroups to finish merges both (log-sum-exp combination: rescale each
+// to the larger maximum) and writes the output.  A smaller item is done whole by
+// half 0; half 1 returns.
 template <int G, int MODE>
 __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb, int kvh,
-                                             char *stage0, char *stage1)
+                                             char *stage0, char *stage1, int half, int *arrival)
 {
     constexpr int BM = 128 / G;
     const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
@@ -132,6 +138,14 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
     const int wg_last_key = off + min(q_len, (qb + 1) * BM) - 1;
     const int n_kt = wg_last_key / BN + 1;
     const int wave_min_kmax = off + qb * BM + (wave * 32) / G;
+    if (half >= 0 && n_kt < kPrefillMinSplitTiles) {
+        if (half == 1)
+            return;   // the whole item belongs to half 0
+        half = -1;
+    }
+    // key tiles of this call: [kt_begin, kt_end)
+    const int kt_begin = half == 1 ? n_kt / 2 : 0;
+    const int kt_end = half == 0 ? n_kt / 2 : n_kt;
 
     const bf16 *ksrc = static_cast<const bf16 *>(MODE == kFlat ? a.k : a.k_cache);
     const bf16 *vsrc = static_cast<const bf16 *>(MODE == kFlat ? a.v : a.v_cache);
@@ -225,10 +239,10 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
     const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
     int32_t tbl[4] = {0, 0, 0, 0};
-    load_tbl(0, tbl);
-    issue_tile(stage0, 0, tbl);
-    if (n_kt > 1)
-        load_tbl(1, tbl);
+    load_tbl(kt_begin, tbl);
+    issue_tile(stage0, kt_begin, tbl);
+    if (kt_begin + 1 < kt_end)
+        load_tbl(kt_begin + 1, tbl);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's copies have landed
     __syncthreads();
 
@@ -239,8 +253,8 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         char *nxt = ST == 0 ? stage1 : stage0;
         // copy of the next tile (the last tile re-copies itself into the stage no step reads
         // again, which keeps this part branch-free so the copies interleave with the MFMAs)
-        issue_tile(nxt, min(kt + 1, n_kt - 1), tbl);
-        load_tbl(min(kt + 2, n_kt - 1), tbl);
+        issue_tile(nxt, min(kt + 1, kt_end - 1), tbl);
+        load_tbl(min(kt + 2, kt_end - 1), tbl);
 
         bf16x8 kf[2][8];
 #pragma unroll
@@ -319,13 +333,84 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         __syncthreads();                      // ... and every wave's part; stage ST is free again
     };
 
-    for (int kt = 0; kt < n_kt; kt += 2) {
+    for (int kt = kt_begin; kt < kt_end; kt += 2) {
         step(std::integral_constant<int, 0>{}, kt);
-        if (kt + 1 < n_kt)
+        if (kt + 1 < kt_end)
             step(std::integral_constant<int, 1>{}, kt + 1);
     }
 
     l += other_half(l, hl);
+    if (half >= 0) {
+        // key-split half: store the partial, count the arrival, and merge if second
+        const int n_lvl = (a.max_seqlen_q + BM - 1) / BM;
+        const int64_t item = ((int64_t)s * n_lvl + qb) * Hkv + kvh;
+        constexpr int kWords = (int)(kPrefillPartBytes / 4);
+        constexpr int kOWords = 4 * 32 * 64;
+        uint32_t *mine = static_cast<uint32_t *>(a.ws_part) + (item * 2 + half) * kWords;
+        const float inv = l > 0.f ? 1.f / l : 0.f;   // a column may see no key of this half
+        // The partial and the counter use device-scope (coherent across XCDs) relaxed
+        // atomic stores and loads, which go through to the coherent level instead of
+        // staying in one XCD's L2; vmcnt(0) makes every store complete before the
+        // arrival is counted.  (A device-scope fence would instead write back and
+        // invalidate the whole L2 of the XCD, evicting the K/V tiles of every other
+        // workgroup there.)
+        auto st = [](uint32_t *p, uint32_t v) {
+            __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        auto ldc = [](const uint32_t *p) {
+            return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+#pragma unroll
+        for (int mtd = 0; mtd < 4; ++mtd)
+#pragma unroll
+            for (int v2 = 0; v2 < 8; ++v2) {
+                const auto h2 = __builtin_amdgcn_cvt_pkrtz(acc_o[mtd][2 * v2] * inv, acc_o[mtd][2 * v2 + 1] * inv);
+                st(mine + (wave * 32 + 8 * mtd + v2) * 64 + lane, __builtin_bit_cast(uint32_t, h2));
+            }
+        st(mine + kOWords + (wave * 2 + 0) * 64 + lane, __float_as_uint(m));
+        st(mine + kOWords + (wave * 2 + 1) * 64 + lane, __float_as_uint(l));
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
+        __syncthreads();                      // ... and every wave's, before the arrival counts
+        if (tid == 0)
+            *arrival = __hip_atomic_fetch_add(&a.ws_cnt[item], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const bool second = *arrival == 1;
+        __syncthreads();                      // *arrival is read by all before its next use
+        if (!second)
+            return;
+        const uint32_t *other = static_cast<const uint32_t *>(a.ws_part) + (item * 2 + (1 - half)) * kWords;
+        const float m1 = __uint_as_float(ldc(other + kOWords + (wave * 2 + 0) * 64 + lane));
+        const float l1 = __uint_as_float(ldc(other + kOWords + (wave * 2 + 1) * 64 + lane));
+        const float mm = fmaxf(m, m1);
+        const float w0 = fast_exp2(m - mm);          // own O is unnormalised
+        const float w1 = l1 * fast_exp2(m1 - mm);    // the other's is O / l
+        const float inv2 = 1.f / (l * w0 + w1);
+        if (tid == 0)   // ready for the next call
+            __hip_atomic_store(&a.ws_cnt[item], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (col_valid) {
+            uint16_t *op = static_cast<uint16_t *>(a.out) + ((int64_t)(q0 + qrow) * Hq + head) * D;
+#pragma unroll
+            for (int mtd = 0; mtd < 4; ++mtd)
+#pragma unroll
+                for (int g4 = 0; g4 < 4; ++g4) {
+                    const int d0 = 32 * mtd + 8 * g4 + 4 * hl;
+                    float o[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 2; ++e2) {
+                        const uint32_t w = ldc(other + (wave * 32 + 8 * mtd + 2 * g4 + e2) * 64 + lane);
+                        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+                        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+                        o[2 * e2] = (acc_o[mtd][4 * g4 + 2 * e2] * w0 + lo * w1) * inv2;
+                        o[2 * e2 + 1] = (acc_o[mtd][4 * g4 + 2 * e2 + 1] * w0 + hi * w1) * inv2;
+                    }
+                    uint2 pk;
+                    pk.x = pack_bf16x2(o[0], o[1]);
+                    pk.y = pack_bf16x2(o[2], o[3]);
+                    *reinterpret_cast<uint2 *>(op + d0) = pk;
+                }
+        }
+        return;
+    }
     if (col_valid) {
         const float inv = 1.f / l;
         uint16_t *op = static_cast<uint16_t *>(a.out) + ((int64_t)(q0 + qrow) * Hq + head) * D;
@@ -359,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillArgs a)
     const int qb = n_qblk - 1 - idx / S;
     if (qb * BM >= a.cu_seqlens_q[s + 1] - a.cu_seqlens_q[s])
         return;
-    attend_block<G, MODE>(a, s, qb, kvh, stage0, stage1);
+    attend_block<G, MODE>(a, s, qb, kvh, stage0, stage1, -1, nullptr);
 }
 
 constexpr int kMaxLevels = 1024;   // query-block levels the persistent schedule supports
@@ -380,6 +465,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_persistent_kernel(Prefill
     constexpr int BM = 128 / G;
     __shared__ __attribute__((aligned(1024))) char stage0[STAGEB];
     __shared__ __attribute__((aligned(1024))) char stage1[STAGEB];
+    __shared__ int arrival;                 // key-split mode: the arrival count of an item
     __shared__ int lvl_cnt[kMaxLevels];     // sequences with more than L query blocks
     __shared__ int lvl_start[kMaxLevels];   // rank of the first item of level L
     const int Hkv = a.num_kv_heads, S = a.num_seqs;
@@ -443,7 +529,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_persistent_kernel(Prefill
         }
     }
     __syncthreads();
-    const int total = (lvl_start[0] + lvl_cnt[0] * Hkv);   // non-empty items
+    const int items = lvl_start[0] + lvl_cnt[0] * Hkv;      // non-empty items
+    const int total = a.split ? 2 * items : items;          // key-split mode: two halves each
 
     const int P8 = gridDim.x / 8, x = blockIdx.x % 8, j = blockIdx.x / 8;
     for (int k = 0;; ++k) {
@@ -451,14 +538,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_persistent_kernel(Prefill
         const int rank = 8 * pos + x;
         if (rank >= total)
             break;
-        // level: the smallest L with lvl_start[L] <= rank
+        // the halves of an item take adjacent ranks (so different XCD classes)
+        const int irank = a.split ? rank >> 1 : rank;
+        const int half = a.split ? rank & 1 : -1;
+        // level: the smallest L with lvl_start[L] <= irank
         int lo = 0, hi = n_lvl - 1;
         while (lo < hi) {
             const int mid = (lo + hi) >> 1;
-            if (lvl_start[mid] <= rank) hi = mid; else lo = mid + 1;
+            if (lvl_start[mid] <= irank) hi = mid; else lo = mid + 1;
         }
         const int L = lo;
-        const int within = rank - lvl_start[L];
+        const int within = irank - lvl_start[L];
         const int kvh = within % Hkv;
         int t = within / Hkv;                        // the t-th sequence with more than L blocks
         int s = -1;
@@ -478,7 +568,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_persistent_kernel(Prefill
         }
         if (s < 0)   // cannot happen: the counts and the scan use the same block counts
             break;
-        attend_block<G, MODE>(a, s, L, kvh, stage0, stage1);
+        attend_block<G, MODE>(a, s, L, kvh, stage0, stage1, half, &arrival);
     }
 }
 
@@ -499,16 +589,25 @@ int device_cus()
     return n;
 }
 
+}  // namespace
+int64_t prefill_split_items(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t num_q_heads, int32_t num_kv_heads);
+namespace {
+
 template <int G>
-hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
+hipError_t launch_g(const PrefillArgs &a_in, hipStream_t stream)
 {
+    PrefillArgs a = a_in;
+    if (a.split && prefill_split_items(a.num_seqs, a.max_seqlen_q, a.max_seqlen_k, a.num_q_heads,
+                                       a.num_kv_heads) == 0)
+        a.split = 0;
     constexpr int BM = 128 / G;
     const int64_t n_qblk = (a.max_seqlen_q + BM - 1) / BM;
     const int64_t items = n_qblk * a.num_seqs * a.num_kv_heads;
     const int64_t slots = 2 * (int64_t)device_cus();
     const bool pow2 = (a.block_size & (a.block_size - 1)) == 0;
     const int mode = !a.paged ? kFlat : (a.block_size % BN == 0 && pow2 ? kPagedTile : kPagedRow);
-    if (items > slots && n_qblk <= kMaxLevels) {
+    if ((a.split || items > slots) && n_qblk <= kMaxLevels) {
         const dim3 grid((uint32_t)((slots + 7) / 8 * 8));
         if (mode == kFlat)
             hipLaunchKernelGGL((prefill_persistent_kernel<G, kFlat>), grid, dim3(kThreads), 0, stream, a);
@@ -529,6 +628,27 @@ hipError_t launch_g(const PrefillArgs &a, hipStream_t stream)
 }
 
 }  // namespace
+
+int64_t prefill_split_items(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                            int32_t num_q_heads, int32_t num_kv_heads)
+{
+    if (num_seqs < 1 || max_seqlen_q < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+        return 0;
+    const int g = num_q_heads / num_kv_heads;
+    if (g != 1 && g != 2 && g != 4 && g != 8)
+        return 0;
+    const int64_t bm = 128 / g;
+    const int64_t n_qblk = (max_seqlen_q + bm - 1) / bm;
+    const int64_t items = n_qblk * num_seqs * num_kv_heads;
+    // split only a batch of few, long items: at most one item per two CUs and at least
+    // 2048 keys (32 key tiles) in the longest.  Measured on MI355X (Hq16/Hkv8, one
+    // sequence): q 64 / k 4096 65 -> 46 us, q 512 / k 8192 127 -> 79 us, q 1024 /
+    // k 4096 68 -> 51 us; with more items per CU (8 x U[100,1024] varlen, 4 x 512 over
+    // 4096) or short keys (q = k = 1024) the merge costs more than the shorter
+    // critical path saves.
+    const bool few_long = items * 2 <= (int64_t)device_cus() && max_seqlen_k >= 2048;
+    return (n_qblk <= kMaxLevels && few_long) ? items : 0;
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream)
 {

@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("pa_store_kv", "pa_prefill_varlen", "pa_decode", "pa_decode_workspace_size",
+    for n in ("pa_store_kv", "pa_prefill_varlen", "pa_prefill_varlen_ws",
+              "pa_prefill_workspace_size", "pa_decode", "pa_decode_workspace_size",
               "pa_decode_num_partitions", "pa_slot_mapping", "pa_status_string"):
         assert n in names, n
 
@@ -90,6 +91,47 @@ def test_prefill_validation(lib):
     assert _prefill(lib, bt=FAKE, maxb=4, kc=FAKE, vc=FAKE, bs=0) == SHAPE
     assert _prefill(lib, S=0, q=None) == OK                  # nothing to do
     assert _prefill(lib, mq=0, q=None) == OK
+
+
+PART_BYTES = (4 * 32 * 64 + 4 * 2 * 64) * 4
+
+
+def test_prefill_workspace_size(lib):
+    """Split-mode workspace: two partials and one counter per (query block,
+    sequence, KV head) item, only for few, long items: at most one item per two
+    CUs (the library assumes 256 CUs when no device can be queried) and at least
+    2048 keys."""
+    ws = lib.pa_prefill_workspace_size
+    assert ws(1, 64, 4096, 16, 8, 128) == 8 * (2 * PART_BYTES + 4)          # one block x 8 heads
+    assert ws(2, 512, 4096, 16, 8, 128) == 128 * (2 * PART_BYTES + 4)       # 8 blocks x 2 x 8
+    assert ws(1, 1024, 4096, 8, 8, 128) == 64 * (2 * PART_BYTES + 4)        # g = 1: 128 positions
+    assert ws(4, 512, 4096, 16, 8, 128) == 0    # 256 items: more than one per two CUs
+    assert ws(8, 1024, 1024, 16, 8, 128) == 0   # short keys
+    assert ws(1, 64, 4096, 16, 8, 64) == 0      # unsupported head size
+    assert ws(1, 64, 4096, 24, 8, 128) == 0     # unsupported group
+    assert ws(0, 64, 4096, 16, 8, 128) == 0
+    assert ws(1, 0, 4096, 16, 8, 128) == 0
+    assert ws(1, 4096, 2048, 16, 8, 128) == 0   # max_seqlen_k < max_seqlen_q
+
+
+def _prefill_ws(lib, wsb, ws=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, kc=None, vc=None, bt=None, maxb=0, cuq=FAKE2, cuk=FAKE2,
+             S=1, mq=64, mk=4096, hq=16, hkv=8, d=128, bs=256, scale=0.088, out=FAKE)
+    a.update(kw)
+    return lib.pa_prefill_varlen_ws(a["q"], a["k"], a["v"], a["kc"], a["vc"], a["bt"], a["maxb"],
+                                    a["cuq"], a["cuk"], a["S"], a["mq"], a["mk"], a["hq"], a["hkv"],
+                                    a["d"], a["bs"], ctypes.c_float(a["scale"]), ws, wsb,
+                                    a["out"], None)
+
+
+def test_prefill_ws_validation(lib):
+    need = lib.pa_prefill_workspace_size(1, 64, 4096, 16, 8, 128)
+    assert need > 0
+    assert _prefill_ws(lib, need - 1) == WORKSPACE
+    assert _prefill_ws(lib, need, ws=None) == NULL
+    assert _prefill_ws(lib, need, ws=ctypes.c_void_p(0x10008)) == UNSUPPORTED   # misaligned
+    assert _prefill_ws(lib, need, d=64) == UNSUPPORTED     # checked before the workspace
+    assert _prefill_ws(lib, 0, S=0, q=None, ws=None) == OK
 
 
 def _decode(lib, **kw):

@@ -34,7 +34,7 @@ def _wl(**kw):
     return workloads.synthetic(**kw)
 
 
-def _gpu_synthetic(pa, wl, decode_too=False, partition_size=0):
+def _gpu_synthetic(pa, wl, decode_too=False, partition_size=0, workspace=None):
     kc = dev_bf16(wl.k_cache)
     vc = dev_bf16(wl.v_cache)
     bt = dev_i32(wl.block_tables)
@@ -48,11 +48,12 @@ def _gpu_synthetic(pa, wl, decode_too=False, partition_size=0):
     if ph.paged:
         out = pa.pa_prefill_varlen(q, None, None, kc, vc, bt, dev_i32(ph.cu_seqlens_q),
                                    dev_i32(cu_of(ph.seqlens_k)), ph.max_seqlen_q, ph.max_seqlen_k,
-                                   wl.num_kv_heads, wl.scale)
+                                   wl.num_kv_heads, wl.scale, workspace=workspace)
     else:
         out = pa.pa_prefill_varlen(q, dev_bf16(ph.k), dev_bf16(ph.v), None, None, None,
                                    dev_i32(ph.cu_seqlens_q), dev_i32(ph.cu_seqlens_k),
-                                   ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale)
+                                   ph.max_seqlen_q, ph.max_seqlen_k, wl.num_kv_heads, wl.scale,
+                                   workspace=workspace)
     res = {"prefill": host_f64(out), "prefill_bits": host_u16(out)}
     if decode_too:
         dout = pa.pa_decode(q, kc, vc, bt, dev_i32(ph.seqlens_k), int(ph.seqlens_k.max()),
@@ -64,9 +65,9 @@ def _gpu_synthetic(pa, wl, decode_too=False, partition_size=0):
     return res
 
 
-def _check(pa, orc, wl, label, decode_too=False, partition_size=0):
+def _check(pa, orc, wl, label, decode_too=False, partition_size=0, workspace=None):
     log(f"[{label}]")
-    g = _gpu_synthetic(pa, wl, decode_too, partition_size)
+    g = _gpu_synthetic(pa, wl, decode_too, partition_size, workspace)
     o = oracle_pipeline(orc, wl)
     assert np.array_equal(g["k_cache"], o["k_cache"]) and np.array_equal(g["v_cache"], o["v_cache"])
     check_close(g["prefill"], o["prefill"], label + " prefill")
@@ -198,6 +199,59 @@ def test_prefill_many_query_blocks(pa, orc, hq, hkv, bs, paged):
     items = -(-max(q) // (128 // g)) * len(q) * hkv
     assert items > 2 * 256, "the batch must exceed one workgroup per slot"
     _check(pa, orc, wl, f"many blocks Hq={hq} Hkv={hkv} bs={bs} paged={paged}")
+
+
+PART_BYTES = (4 * 32 * 64 + 4 * 2 * 64) * 4   # one half's partial in the prefill workspace
+
+
+SPLIT_CASES = {   # (hq, hkv, block size, paged, peaky, q_lens, k_lens): few, long query blocks
+    "g2-tile": (16, 8, 256, True, False, [1, 200, 320], [100, 2500, 4000]),
+    "g8-row": (8, 1, 16, True, False, [1, 200, 640], [100, 2500, 3000]),
+    "g1-flat-peaky": (8, 8, 64, False, True, [2048], [2048]),
+    "g4-tile-peaky": (32, 8, 64, True, True, [77, 256], [2049, 3000]),
+}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
+def test_prefill_key_split(pa, orc, case):
+    """With a workspace, a batch of few, long query blocks splits every block of
+    at least 4 key tiles into two halves of its key range; the second workgroup
+    to finish merges the two softmax states.  Lengths cover blocks below the
+    split threshold (done whole), odd tile counts, long prefixes, and keys a
+    column cannot see in one half.  The workspace must come back zero-filled
+    (its arrival counters), so a second call on it gives the same result."""
+    hq, hkv, bs, paged, peaky, q, k = SPLIT_CASES[case]
+    wl = _wl(q_lens=q, k_lens=k, num_q_heads=hq, num_kv_heads=hkv, block_size=bs, paged=paged,
+             q_scale=8.0 if peaky else 1.0, v_position=peaky, seed=23)
+    ph = wl.prefill
+    need = pa.pa_prefill_workspace_size(len(q), ph.max_seqlen_q, ph.max_seqlen_k, hq, hkv)
+    assert need > 0, "the batch must be split"
+    ws = pa.pa_prefill_workspace(len(q), ph.max_seqlen_q, ph.max_seqlen_k, hq, hkv)
+    items = need // (2 * PART_BYTES + 4)
+    label = f"key split {case}"
+    g1, o = _check(pa, orc, wl, label, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[items * 2 * PART_BYTES:].count_nonzero()) == 0, "arrival counters not reset"
+    g2, _ = _check(pa, orc, wl, label + " (second call)", workspace=ws)
+    assert int(ws[items * 2 * PART_BYTES:].count_nonzero()) == 0
+    # the unsplit path on the same inputs agrees to the same tolerance
+    g0 = _gpu_synthetic(pa, wl)
+    check_close(g0["prefill"], o["prefill"], label + " unsplit")
+
+
+def test_prefill_workspace_errors(pa):
+    """pa_prefill_varlen_ws rejects a short workspace before launching anything."""
+    from paged_kv_attention_27_amd.binding import PaError
+    wl = _wl(q_lens=[2100, 20], k_lens=[2100, 20], paged=False, num_q_heads=2, num_kv_heads=2,
+             seed=24)
+    ph = wl.prefill
+    need = pa.pa_prefill_workspace_size(2, ph.max_seqlen_q, ph.max_seqlen_k, 2, 2)
+    assert need > 0
+    short = torch.zeros(need - 4, dtype=torch.uint8, device="cuda")
+    with pytest.raises(PaError):
+        pa.pa_prefill_varlen(dev_bf16(ph.q), dev_bf16(ph.k), dev_bf16(ph.v), None, None, None,
+                             dev_i32(ph.cu_seqlens_q), dev_i32(ph.cu_seqlens_k), ph.max_seqlen_q,
+                             ph.max_seqlen_k, 2, wl.scale, workspace=short)
 
 
 # ------------------------------------------------------------------ decode
