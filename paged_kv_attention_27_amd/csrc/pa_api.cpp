@@ -165,6 +165,8 @@ int prefill_impl(const void *q, const void *k, const void *v, const void *k_cach
         return PA_ERR_SHAPE;
     if (head_dim != kHeadDim || !group_supported(num_q_heads, num_kv_heads))
         return PA_ERR_UNSUPPORTED;
+    if (num_kv_heads >= 65536)   // a K/V row (Hkv * 256 B) must stay below 2^24 bytes
+        return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0 || max_seqlen_q == 0)
         return PA_OK;
     if (!q || !out || !cu_seqlens_q || !cu_seqlens_k)

@@ -208,7 +208,8 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         const char *vb = reinterpret_cast<const char *>(vsrc) + tile_row0 * row_bytes;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t o = coff[j] - (uint32_t)max(16 * wave + 4 * j + lsub - last, 0) * row_bytes;
+            // rows past the last key re-read it (< 64 rows; a 24-bit multiply runs at full rate)
+            const uint32_t o = coff[j] - __umul24((uint32_t)max(16 * wave + 4 * j + lsub - last, 0), row_bytes);
             char *dst = stage + (16 * wave + 4 * j) * ROWB;
             copy16_to_lds(kb, o, dst);
             copy16_to_lds(vb, o, dst + TILEB);
@@ -280,13 +281,14 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
 
         const int kbase = kt * BN;
         if (kbase + BN - 1 > wave_min_kmax) {
+            // value v of block mt holds key kbase + 32 mt + 8 (v / 4) + 4 hl + v % 4: compare
+            // its constant part with one per-lane limit
+            const int lim = kmax - kbase - 4 * hl;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = kbase + 32 * mt + 8 * (v >> 2) + 4 * hl + (v & 3);
-                    if (key > kmax) sacc[mt][v] = -INFINITY;
-                }
+                for (int v = 0; v < 16; ++v)
+                    if (32 * mt + 8 * (v >> 2) + (v & 3) > lim) sacc[mt][v] = -INFINITY;
         }
 
         float tmax = sacc[0][0];
