@@ -19,7 +19,9 @@ The same run also measures, as sub-objects of the JSON line:
     algorithmic work (two GEMMs over visible query/key pairs only);
   * ``decode_long``: the 16 x 32768-token decode (Hq=32, group of 4);
   * ``decode_head_ratios``: the 256-sequence decode at 8 Q heads over 8, 2
-    and 1 KV heads (MHA, GQA, MQA: KV bytes 8:2:1).
+    and 1 KV heads (MHA, GQA, MQA: KV bytes 8:2:1);
+  * ``prefill_long_chunk``: 64 new queries over 4096 keys, with and without
+    the key-split workspace.
 ``roofline`` is the dominant kernel of the headline step (the split-K decode
 pass with the fused store), timed alone with HIP events on its own stream;
 ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of the same
@@ -385,6 +387,25 @@ def main():
         result["decode_head_ratios"] = {
             "workload": "256 seqs, ctx U[128,4096], Hq 8 over Hkv 8/2/1, block 256; fused step, HIP graph",
             **ratios}
+
+        # a short chunk over a long cached prefix: few, long query blocks, where the
+        # workspace call splits each block's key range between two workgroups
+        cwl = workloads.synthetic(q_lens=[64], k_lens=[4096], block_size=256, seed=27100,
+                                  name="chunk64_over_4096")
+        cs = PrefillSetup(torch, pa, cwl)
+        _, t_split = cs.time(max(args.steps, 10), args.warmup)
+        ws, cs.ws = cs.ws, None
+        _, t_plain = cs.time(max(args.steps, 10), args.warmup)
+        cs.ws = ws
+        result["prefill_long_chunk"] = {
+            "workload": "1 seq: 64 new queries over a 4032-token cached prefix (k_len 4096), "
+                        "Hq16/Hkv8/d128, block 256, keys read through the pools",
+            "key_split": cs.split, "ms_attention_split": round(float(t_split), 5),
+            "ms_attention_unsplit": round(float(t_plain), 5),
+            "speedup": round(float(t_plain / t_split), 3)}
+        log(f"64 queries over 4096 keys: {t_split * 1e3:.1f} us with the key split, "
+            f"{t_plain * 1e3:.1f} us without")
+        del cs, cwl
 
     if args.calibrate_copy:
         n = 1 << 29   # bf16 elements: 1 GiB read + 1 GiB written per copy
