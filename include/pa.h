@@ -157,18 +157,21 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t
 /*
  * pa_prefill_varlen with a workspace: the same operation and arguments, plus
  * a key split for batches of few, long query blocks (see
- * pa_prefill_workspace_size; there the longest blocks set the time).  Each query block with at least 4 key tiles of
- * 64 keys is then computed as two halves of its key range by two workgroups;
+ * pa_prefill_workspace_size; there the longest blocks set the time).  Each
+ * query block with at least 4 key tiles of 64 keys is then computed as two
+ * halves of its key range by two workgroups;
  * the second to finish merges the two partial softmax states, rescaling both
  * to the larger running maximum (the log-sum-exp combination that lets the
  * blocked computation of [Atlas] ch.22 avoid the full score matrix).  Results
  * differ from pa_prefill_varlen only by rounding (the partials are stored as
  * fp16 O / l with fp32 max and sum).
  *
- * workspace  (device) >= pa_prefill_workspace_size(...) bytes, 16-byte aligned,
- *            zero-filled before its first use; every call leaves it zero-filled
- *            again (its arrival counters), so it can be reused without clearing.
- *            Calls that share a workspace must not overlap in time (one stream).
+ * workspace  (device) >= pa_prefill_workspace_size(...) bytes (sized on the
+ *            device the call runs on), 16-byte aligned, zero-filled before its
+ *            first use.  It holds the partials and, at its end, one arrival
+ *            counter per item; every call returns the counters to zero, so the
+ *            buffer can be reused without clearing.  Calls that share a
+ *            workspace must not overlap in time (issue them on one stream).
  * Errors as pa_prefill_varlen, plus PA_ERR_WORKSPACE (workspace_bytes too small)
  * and PA_ERR_NULL (workspace NULL while one is needed).
  */
