@@ -121,12 +121,15 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
             const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(bt_row[lb]) * bs + (cs - lb * bs);
             const bf16 *kb = kc + row0 * row_elems + lane_off;
             const bf16 *vb = vc + row0 * row_elems + lane_off;
+            // all K rows first, then all V rows: the scores need only K, so they can start
+            // while the V rows are still in flight, and K and V requests (same offsets in
+            // two pools) are not interleaved (measured ~4 % faster in a read-only probe)
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const bool ok = base + u < t_stop;
-                kr[u] = ok ? ld(kb + u * row_elems) : make_uint4(0, 0, 0, 0);
-                vr[u] = ok ? ld(vb + u * row_elems) : make_uint4(0, 0, 0, 0);
-            }
+            for (int u = 0; u < U; ++u)
+                kr[u] = base + u < t_stop ? ld(kb + u * row_elems) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                vr[u] = base + u < t_stop ? ld(vb + u * row_elems) : make_uint4(0, 0, 0, 0);
         } else {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
