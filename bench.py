@@ -5,7 +5,8 @@
 
 Workload of the headline line: batched paged decode, 256 sequences with
 context lengths U[128, 4096] (new token included), Hq=16 / Hkv=8 / d=128,
-block size 256, 4096-block pool, seeded N(0,1) inputs.  One step is one decode
+block size 256, 4096-block pool, seeded N(0,1) inputs; the K and V pools share
+one allocation, placed as pa_kv_pool_layout gives.  One step is one decode
 round: store the 256 new K/V rows and attend over every history
 (pa_decode_store: the store is fused into the attention kernel, plus the
 reduce pass when a context is split), captured once in a HIP graph and
@@ -78,6 +79,15 @@ def dev_i32(torch, a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
+def dev_pools(torch, pa, wl):
+    """The workload's K/V pools in one device allocation, V placed as
+    pa_kv_pool_layout gives (384 bytes modulo 1 KiB past K)."""
+    kc, vc = pa.alloc_kv_pools(*wl.k_cache.shape)
+    kc.copy_(dev_bf16(torch, wl.k_cache))
+    vc.copy_(dev_bf16(torch, wl.v_cache))
+    return kc, vc
+
+
 def decode_kv_bytes(wl, ctx):
     return int(np.sum(ctx.astype(np.int64))) * wl.num_kv_heads * wl.head_dim * 2 * 2
 
@@ -95,8 +105,7 @@ class DecodeSetup:
     def __init__(self, torch, pa, wl, partition_size):
         self.torch, self.pa, self.wl = torch, pa, wl
         ph = wl.decode
-        self.kc = dev_bf16(torch, wl.k_cache)
-        self.vc = dev_bf16(torch, wl.v_cache)
+        self.kc, self.vc = dev_pools(torch, pa, wl)
         self.bt = dev_i32(torch, wl.block_tables)
         self.ctx = dev_i32(torch, ph.seqlens_k)
         self.q = dev_bf16(torch, ph.q)
@@ -177,8 +186,7 @@ class PrefillSetup:
     def __init__(self, torch, pa, wl):
         self.torch, self.pa, self.wl = torch, pa, wl
         ph = wl.prefill
-        self.kc = dev_bf16(torch, wl.k_cache)
-        self.vc = dev_bf16(torch, wl.v_cache)
+        self.kc, self.vc = dev_pools(torch, pa, wl)
         self.bt = dev_i32(torch, wl.block_tables)
         self.stream = torch.cuda.Stream()
         if wl.prefix is not None:   # the cached prefix is stored once, before timing
@@ -315,7 +323,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "batched paged decode: 256 seqs, ctx U[128,4096] incl. new token, "
-                               "Hq16/Hkv8/d128, block 256, 4096-block pool; step = fused store "
+                               "Hq16/Hkv8/d128, block 256, 4096-block pool (K and V pools in one "
+                               "allocation, V at +384 B mod 1 KiB); step = fused store "
                                "+ split-K attention (+ reduce when partitioned), HIP graph",
                    "num_seqs": wl.num_seqs, "sum_context": int(wl.decode.seqlens_k.sum()),
                    "kv_bytes_per_step": dset.bytes, "partition_tokens":

@@ -107,6 +107,27 @@ int pa_store_kv(const void *k, const void *v, void *k_cache, void *v_cache,
                 hipStream_t stream);
 
 /*
+ * Placement of the two pools in one reservation.  The engine reserves the
+ * whole KV pool once, up front, and afterwards only changes which blocks the
+ * requests hold ([Course] "THE IMPORTANT DETAILS" item 02).  When k_cache and
+ * v_cache share one allocation, this gives its size and where v_cache starts:
+ * k_cache at byte 0, v_cache after it at an offset whose remainder modulo
+ * 1024 bytes is 384.  The kernels read a token's K row and V row at the same
+ * time; with the two pools at the same address modulo 1 KiB those reads land
+ * in the same part of the HBM interleave and the decode loses bandwidth
+ * (measured on MI355X: 256-sequence decode 383 -> 354 us, 16 x 32768-token
+ * decode 359 -> 346 us).  Any other placement of 16-byte aligned pools is
+ * equally correct for every entry point; only the speed changes.
+ *
+ * v_offset  (host, out) byte offset of v_cache from the start of the allocation
+ * Returns the allocation size in bytes (k_cache bytes + padding + v_cache
+ * bytes), or 0 with *v_offset untouched if v_offset is NULL, a size is not
+ * positive, or the size does not fit in a size_t.
+ */
+size_t pa_kv_pool_layout(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, size_t *v_offset);
+
+/*
  * Variable-length causal prefill attention.
  *
  * For sequence s: q_len = cu_seqlens_q[s+1] - cu_seqlens_q[s] query rows and

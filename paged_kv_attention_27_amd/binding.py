@@ -47,6 +47,8 @@ def load():
     lib.pa_slot_mapping.argtypes = [_P, _P, _I, _P, _I, _I, _P, _I]
     lib.pa_store_kv.restype = ctypes.c_int
     lib.pa_store_kv.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+    lib.pa_kv_pool_layout.restype = ctypes.c_size_t
+    lib.pa_kv_pool_layout.argtypes = [_I, _I, _I, _I, ctypes.POINTER(ctypes.c_size_t)]
     lib.pa_prefill_varlen.restype = ctypes.c_int
     lib.pa_prefill_varlen.argtypes = [_P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                       _I, _I, ctypes.c_float, _P, _P]
@@ -139,6 +141,28 @@ def pa_store_kv(k, v, k_cache, v_cache, slot_mapping, stream=None):
                             _dev(slot_mapping, torch.int32, "slot_mapping"),
                             T, NB, bs, Hkv, d, _stream(stream))
     _check("pa_store_kv", st)
+
+
+def pa_kv_pool_layout(num_blocks, block_size, num_kv_heads, head_dim):
+    """(allocation bytes, byte offset of v_cache) for both pools in one allocation."""
+    off = ctypes.c_size_t(0)
+    total = load().pa_kv_pool_layout(int(num_blocks), int(block_size), int(num_kv_heads),
+                                     int(head_dim), ctypes.byref(off))
+    if total == 0:
+        raise ValueError("pa_kv_pool_layout: invalid or oversized pool shape")
+    return int(total), int(off.value)
+
+
+def alloc_kv_pools(num_blocks, block_size, num_kv_heads, head_dim, device="cuda"):
+    """k_cache and v_cache [num_blocks, block_size, num_kv_heads, head_dim] bf16, placed in
+    one device allocation as pa_kv_pool_layout gives (contents uninitialised)."""
+    total, off = pa_kv_pool_layout(num_blocks, block_size, num_kv_heads, head_dim)
+    shape = (num_blocks, block_size, num_kv_heads, head_dim)
+    n = num_blocks * block_size * num_kv_heads * head_dim * 2
+    buf = torch.empty(total, dtype=torch.uint8, device=device)
+    k_cache = buf[:n].view(torch.bfloat16).view(shape)
+    v_cache = buf[off:off + n].view(torch.bfloat16).view(shape)
+    return k_cache, v_cache
 
 
 def pa_prefill_workspace_size(num_seqs, max_seqlen_q, max_seqlen_k, num_q_heads, num_kv_heads,

@@ -2,6 +2,7 @@
 // include/pa.h): host-side argument checks, kernel selection and launch.
 // Nothing here reads device memory, allocates, or synchronises, so every
 // device entry point can be captured into a HIP graph.
+#include <initializer_list>
 #include <math.h>
 #include <stdint.h>
 
@@ -130,6 +131,26 @@ int pa_store_kv(const void *k, const void *v, void *k_cache, void *v_cache,
     hipError_t e = pa::launch_store_kv(k, v, k_cache, v_cache, slot_mapping, num_tokens,
                                        (int32_t)row, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;
+}
+
+size_t pa_kv_pool_layout(int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, size_t *v_offset)
+{
+    // v_cache starts 384 bytes past a 1 KiB boundary after k_cache (the pools then
+    // differ modulo 1 KiB, which keeps a row's K and V reads apart in the HBM interleave)
+    constexpr uint64_t kAlign = 1024, kShift = 384;
+    if (!v_offset || num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1)
+        return 0;
+    uint64_t pool = 2u;   // bytes of one pool, with every product checked for overflow
+    for (int32_t f : {num_blocks, block_size, num_kv_heads, head_dim})
+        if (__builtin_mul_overflow(pool, (uint64_t)f, &pool))
+            return 0;
+    if (pool > (uint64_t)SIZE_MAX / 2 - 2 * kAlign)
+        return 0;
+    const uint64_t voff = (pool + kAlign - 1) / kAlign * kAlign + kShift;
+    const uint64_t total = voff + pool;
+    *v_offset = (size_t)voff;
+    return (size_t)total;
 }
 
 size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,

@@ -30,6 +30,16 @@ def dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
+def dev_pools(pa, wl):
+    """The workload's initial pools on the GPU in one allocation, placed as
+    pa_kv_pool_layout recommends (the layout the benchmark times)."""
+    nb, bs, hkv, d = wl.k_cache.shape
+    kc, vc = pa.alloc_kv_pools(nb, bs, hkv, d)
+    kc.copy_(dev_bf16(wl.k_cache))
+    vc.copy_(dev_bf16(wl.v_cache))
+    return kc, vc
+
+
 def host_u16(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
@@ -59,10 +69,13 @@ def check_close(gpu, ref, label, max_tol=PARITY_MAX, mean_tol=PARITY_MEAN):
     return mx, mean
 
 
-def gpu_pipeline(pa, wl, partition_size=0, keep_pools=True):
-    """Run every phase of ``wl`` through libpa.  Returns host results."""
-    kc = dev_bf16(wl.k_cache)
-    vc = dev_bf16(wl.v_cache)
+def gpu_pipeline(pa, wl, partition_size=0, keep_pools=True, one_allocation=True):
+    """Run every phase of ``wl`` through libpa, with both pools in one allocation
+    (pa_kv_pool_layout) or in two.  Returns host results."""
+    if one_allocation:
+        kc, vc = dev_pools(pa, wl)
+    else:
+        kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
     bt = dev_i32(wl.block_tables)
     res = {}
 

@@ -68,6 +68,26 @@ def test_store_validation(lib):
     assert st(FAKE, FAKE, FAKE, FAKE, FAKE, 5, 2**20, 2**12, 8, 128, None) == SHAPE  # slots overflow
 
 
+def test_kv_pool_layout(lib):
+    """One allocation for both pools: k_cache at byte 0, v_cache after it at an
+    offset of 384 modulo 1 KiB (16-byte aligned, no overlap); invalid or
+    oversized shapes return 0 and leave the offset untouched."""
+    off = ctypes.c_size_t(7)
+    for nb, bs, hkv, d in [(4096, 256, 8, 128), (2048, 256, 8, 128), (16, 256, 8, 128),
+                           (3, 1, 1, 8), (5, 768, 2, 128), (1, 1, 1, 1)]:
+        total = lib.pa_kv_pool_layout(nb, bs, hkv, d, ctypes.byref(off))
+        pool = nb * bs * hkv * d * 2
+        assert off.value % 1024 == 384 and off.value % 16 == 0
+        assert pool <= off.value < pool + 1024 + 384
+        assert total == off.value + pool
+    for bad in [(0, 256, 8, 128), (16, 0, 8, 128), (16, 256, -1, 128), (16, 256, 8, 0),
+                (2**31 - 1, 2**31 - 1, 2**31 - 1, 2**31 - 1)]:
+        off.value = 7
+        assert lib.pa_kv_pool_layout(*bad, ctypes.byref(off)) == 0
+        assert off.value == 7
+    assert lib.pa_kv_pool_layout(16, 256, 8, 128, None) == 0
+
+
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, kc=None, vc=None, bt=None, maxb=0, cuq=FAKE2, cuk=FAKE2,
              S=2, mq=10, mk=10, hq=16, hkv=8, d=128, bs=256, scale=0.088, out=FAKE)

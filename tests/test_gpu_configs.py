@@ -1,8 +1,10 @@
 """GPU parity on the five workload configurations, through the C-ABI.
 
 For each configuration the library and the oracle run the same phases on the
-same seeded inputs; the pools after every store must be bit-identical (whole
-pools compared, so a stray write anywhere fails) and the attention outputs
+same seeded inputs, with K and V pools placed in one allocation as
+pa_kv_pool_layout gives (the layout the benchmark times); the pools after
+every store must be bit-identical (whole pools compared, so a stray write
+anywhere fails) and the attention outputs
 must satisfy max|err| <= 2e-2 and mean|err| <= 2e-3 against the fp64 oracle.
 """
 import gc
@@ -35,15 +37,31 @@ def test_config_parity(cfg, orc):
     gc.collect()
 
 
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_pool_placement_bit_identical(cfg):
+    """The pools' placement changes only speed: two separate allocations and the
+    one-allocation layout give the same output and pool bits."""
+    import paged_kv_attention_27_amd as pa
+    from paged_kv_attention_27_amd import workloads
+    wl = workloads.make(cfg)
+    log(f"[config {cfg}] two allocations vs one")
+    a = gpu_pipeline(pa, wl, one_allocation=False)
+    b = gpu_pipeline(pa, wl, one_allocation=True)
+    assert a.keys() == b.keys()
+    for key in a:
+        if key.endswith("_bits") or key.endswith("_cache"):
+            assert np.array_equal(a[key], b[key]), key
+
+
 @pytest.mark.parametrize("cfg", [1, 4, 5])
 def test_config_decode_fused(cfg, orc):
     """The fused store + decode step on the decode configurations."""
     import paged_kv_attention_27_amd as pa
     from paged_kv_attention_27_amd import workloads
-    from pipelines import dev_bf16, dev_i32, host_f64, host_u16, prefix_tables
+    from pipelines import dev_bf16, dev_i32, dev_pools, host_f64, host_u16, prefix_tables
     log(f"[config {cfg}] fused decode: generating inputs")
     wl = workloads.make(cfg)
-    kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
+    kc, vc = dev_pools(pa, wl)
     okc, ovc = wl.k_cache.copy(), wl.v_cache.copy()
     bs = wl.block_size
     for ph in (wl.prefix, wl.prefill):   # config 1 stores its prompt first
@@ -71,10 +89,10 @@ def test_head_ratio_decode_parity(hkv, orc):
     """Hq = 8 over Hkv = 8 / 2 / 1 at the batched-decode size (fused step vs oracle)."""
     import paged_kv_attention_27_amd as pa
     from paged_kv_attention_27_amd import workloads
-    from pipelines import dev_bf16, dev_i32, host_f64, host_u16
+    from pipelines import dev_bf16, dev_i32, dev_pools, host_f64, host_u16
     log(f"[Hq8/Hkv{hkv}] generating inputs")
     wl = workloads.head_ratio_decode(hkv)
-    kc, vc = dev_bf16(wl.k_cache), dev_bf16(wl.v_cache)
+    kc, vc = dev_pools(pa, wl)
     okc, ovc = wl.k_cache.copy(), wl.v_cache.copy()
     ph = wl.decode
     slots = pa.pa_slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables, wl.block_size)
