@@ -39,6 +39,27 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr float kLazyTau = 8.0f;   // log2 growth of a running max tolerated before rescaling
 
+// v[i] += v[i] from the lane the DPP control CTRL selects, for N independent values
+template <int CTRL, int N>
+__device__ __forceinline__ void dpp_add_all(float *v)
+{
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                    0, __builtin_bit_cast(int, v[i]), CTRL, 0xF, 0xF, false));
+}
+
+// row16_sum of N independent values, one DPP step across all of them at a time
+// (each lane of a 16-lane row ends with the row's bit-identical total)
+template <int N>
+__device__ __forceinline__ void row16_sum_all(float *v)
+{
+    dpp_add_all<0xB1, N>(v);    // quad_perm [1,0,3,2]
+    dpp_add_all<0x4E, N>(v);    // quad_perm [2,3,0,1]
+    dpp_add_all<0x141, N>(v);   // row_half_mirror
+    dpp_add_all<0x140, N>(v);   // row_mirror
+}
+
 template <int G, int U, bool CHUNK_IN_BLOCK, bool FUSED_STORE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 {
@@ -146,24 +167,32 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
             }
         }
 
-        // raw scores q.k (all 16 lanes of a group hold the bit-identical total)
+        // raw scores q.k (all 16 lanes of a group hold the bit-identical total).  The
+        // partial dot products of every key and head are formed first and then reduced
+        // one DPP step at a time across all of them, so the steps' latencies overlap
+        // (summed whatever the key's validity: its lanes hold zeros then).
         float sc[G][U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                float d0 = 0.f, d1 = 0.f;
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][0]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].x), d0, false);
+                d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][1]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].y), d1, false);
+                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][2]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].z), d0, false);
+                d1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][3]),
+                                                     __builtin_bit_cast(bf16x2, kr[u].w), d1, false);
+                sc[h][u] = d0 + d1;
+            }
+        row16_sum_all<G * U>(&sc[0][0]);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const bool valid = base + u < t_stop;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-                float d0 = 0.f;
-                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][0]),
-                                                     __builtin_bit_cast(bf16x2, kr[u].x), d0, false);
-                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][1]),
-                                                     __builtin_bit_cast(bf16x2, kr[u].y), d0, false);
-                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][2]),
-                                                     __builtin_bit_cast(bf16x2, kr[u].z), d0, false);
-                d0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qw[h][3]),
-                                                     __builtin_bit_cast(bf16x2, kr[u].w), d0, false);
-                sc[h][u] = valid ? row16_sum(d0) : -INFINITY;
-            }
+            for (int h = 0; h < G; ++h) sc[h][u] = valid ? sc[h][u] : -INFINITY;
         }
 
         // lazy running max: rescale only when some head's max grew by more than 2^8
