@@ -12,7 +12,10 @@
 //     covers 4*U keys and keeps 2*U loads per lane in flight.  When the block
 //     and partition sizes are multiples of 4*U the iteration's keys share one
 //     block, found by one scalar table lookup.  Scores use v_dot2_f32_bf16 and a 4-step DPP row
-//     reduction; weighted values use v_dot2_f32_bf16 over pairs of keys, with
+//     reduction (groups of 8 Q heads: a 16x16x32 bf16 MFMA per 16 keys and 32
+//     head-dim elements, the weights then broadcast from the score lanes to
+//     their lane groups with DPP row broadcasts); weighted values use
+//     v_dot2_f32_bf16 over pairs of keys, with
 //     the weights rounded to bf16 (the same rounding the prefill MFMA applies).
 //     The softmax runs online in the log2 domain with a lazily updated running
 //     max (rescale only when it grows by more than 2^8).  Each wave keeps its
@@ -47,6 +50,22 @@ __device__ __forceinline__ void dpp_add_all(float *v)
     for (int i = 0; i < N; ++i)
         v[i] += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                     0, __builtin_bit_cast(int, v[i]), CTRL, 0xF, 0xF, false));
+}
+
+// value of lane h of this lane's 16-lane row (DPP row_newbcast); h is a constant
+// once the caller's loop is unrolled
+__device__ __forceinline__ int row_bcast(int v, int h)
+{
+    switch (h) {
+    case 0: return __builtin_amdgcn_update_dpp(0, v, 0x150, 0xF, 0xF, false);
+    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x151, 0xF, 0xF, false);
+    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x152, 0xF, 0xF, false);
+    case 3: return __builtin_amdgcn_update_dpp(0, v, 0x153, 0xF, 0xF, false);
+    case 4: return __builtin_amdgcn_update_dpp(0, v, 0x154, 0xF, 0xF, false);
+    case 5: return __builtin_amdgcn_update_dpp(0, v, 0x155, 0xF, 0xF, false);
+    case 6: return __builtin_amdgcn_update_dpp(0, v, 0x156, 0xF, 0xF, false);
+    default: return __builtin_amdgcn_update_dpp(0, v, 0x157, 0xF, 0xF, false);
+    }
 }
 
 // row16_sum of N independent values, one DPP step across all of them at a time
@@ -102,11 +121,33 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     const int64_t row_elems = (int64_t)Hkv * D;
 
     const bf16 *q = static_cast<const bf16 *>(a.q);
+    // q in the dot-product layout: lane c of every lane group holds q[8c .. 8c+8)
     uint32_t qw[G][4];
+    auto load_qw = [&]() {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)s * Hq + kvh * G + h) * D + 8 * c);
-        qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
+        for (int h = 0; h < G; ++h) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)s * Hq + kvh * G + h) * D + 8 * c);
+            qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
+        }
+    };
+
+    // groups of 8 Q heads: the scores are an MFMA, S = K Q^T with 16 keys (M) x 16
+    // columns (N: the G heads, the rest zero) x 32 head-dim elements (K) per
+    // instruction.  B operand: lane l holds Q[head l%16][32 kq + 8 (l/16) .. +8].
+    // (Measured on MI355X: MQA step 135 -> 90 us.  For groups of 4 the dot-product
+    // path stays: its K loads read 4 whole rows per instruction where the MFMA
+    // layout reads 16 half lines, and the 16 x 32768 decode lost 2 % with it.)
+    constexpr bool kMfmaQK = G >= 8;
+    bf16x8 qt[4];
+    if constexpr (!kMfmaQK) {
+        load_qw();
+    } else {
+        const int hcol = lane & 15;
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq)
+            qt[kq] = hcol < G ? *reinterpret_cast<const bf16x8 *>(
+                                    q + ((int64_t)s * Hq + kvh * G + hcol) * D + 32 * kq + 8 * r)
+                              : bf16x8{};
     }
 
     float m[G], l[G], acc[G][8];
@@ -134,6 +175,133 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
     };
     for (int ch = wave; ch < n_chunks; ch += kWaves) {
         const int cs = t_begin + ch * kChunk;
+        if constexpr (kMfmaQK) {
+            static_assert(U == 8, "the MFMA score path takes 32-key chunks");
+            // K as the MFMA A operand: for key half kb and head-dim chunk kc, lane l holds
+            // K[key cs + 16 kb + l%16][32 kc + 8 (l/16) .. +8] (one instruction reads 16 rows
+            // x 64 contiguous bytes).  V in the weighting layout: lane group r owns keys
+            // 4r + i and 16 + 4r + i (i < 4), the same keys the score accumulators of its
+            // rows hold, so the weights move to it with row broadcasts.
+            const int kl = lane & 15;
+            uint4 kf[2][4], vr[8];
+            auto vkey = [&](int u) { return (u & 3) + 4 * r + 16 * (u >> 2); };
+            if (CHUNK_IN_BLOCK) {
+                const int lb = __builtin_amdgcn_readfirstlane(shift >= 0 ? (cs >> shift) : (cs / bs));
+                const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(bt_row[lb]) * bs + (cs - lb * bs);
+                const bf16 *kb0 = kc + row0 * row_elems + kvh * D;
+                const bf16 *vb0 = vc + row0 * row_elems + kvh * D + 8 * c;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        kf[kb][q4] = cs + 16 * kb + kl < t_stop
+                                         ? ld(kb0 + (16 * kb + kl) * row_elems + 32 * q4 + 8 * r)
+                                         : make_uint4(0, 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    vr[u] = cs + vkey(u) < t_stop ? ld(vb0 + vkey(u) * row_elems) : make_uint4(0, 0, 0, 0);
+            } else {
+                auto row_of = [&](int j) {
+                    const int lb = shift >= 0 ? (j >> shift) : (j / bs);
+                    return ((int64_t)bt_row[lb] * bs + (j - lb * bs)) * row_elems + kvh * D;
+                };
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int j = cs + 16 * kb + kl;
+                    const int64_t o = j < t_stop ? row_of(j) : 0;
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        kf[kb][q4] = j < t_stop ? ld(kc + o + 32 * q4 + 8 * r) : make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int j = cs + vkey(u);
+                    vr[u] = j < t_stop ? ld(vc + row_of(j) + 8 * c) : make_uint4(0, 0, 0, 0);
+                }
+            }
+
+            // scores: lane l holds S[key cs + 16 kb + 4 (l/16) + i][head l%16], i < 4
+            f32x4 sacc[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8, kf[kb][q4]), qt[q4], sacc[kb], 0, 0, 0);
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (cs + 16 * kb + 4 * r + i >= t_stop) sacc[kb][i] = -INFINITY;
+                    mx = fmaxf(mx, sacc[kb][i]);
+                }
+            mx = fmaxf(mx, shfl_xor_f(mx, 16));
+            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            // lanes h, h+16, h+32, h+48 now hold head h's chunk maximum
+            bool grow_any = false;
+            float mcand[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                mcand[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), h)) * sl2;
+                grow_any |= mcand[h] > m[h] + kLazyTau;
+            }
+            if (grow_any) {   // wave-uniform: the maxima are read from lanes
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float mnew = fmaxf(m[h], mcand[h]);
+                    const float alpha = fast_exp2(m[h] - mnew);
+                    m[h] = mnew;
+                    l[h] *= alpha;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[h][e] *= alpha;
+                }
+            }
+            // weights in the score layout (this lane's head is l%16; columns past G unused),
+            // rounded to bf16 in pairs of consecutive keys
+            float mh = m[0];
+#pragma unroll
+            for (int h = 1; h < G; ++h) mh = kl == h ? m[h] : mh;
+            uint32_t pw[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const float p0 = fast_exp2(fmaf(sacc[kb][2 * pr], sl2, -mh));
+                    const float p1 = fast_exp2(fmaf(sacc[kb][2 * pr + 1], sl2, -mh));
+                    const bf16x2 pp = {(bf16)p0, (bf16)p1};
+                    pw[kb][pr] = __builtin_bit_cast(uint32_t, pp);
+                }
+            // weighted values: keys (u, u+1) = (4 kb + 2 pr, +1) of this lane group; the
+            // weights of head h come from lane h of the row (DPP row broadcast)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int u = 4 * kb + 2 * pr;
+                    uint32_t vlo[4], vhi[4];
+                    const uint32_t w0[4] = {vr[u].x, vr[u].y, vr[u].z, vr[u].w};
+                    const uint32_t w1[4] = {vr[u + 1].x, vr[u + 1].y, vr[u + 1].z, vr[u + 1].w};
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        vlo[w] = __builtin_amdgcn_perm(w1[w], w0[w], 0x05040100u);
+                        vhi[w] = __builtin_amdgcn_perm(w1[w], w0[w], 0x07060302u);
+                    }
+#pragma unroll
+                    for (int h = 0; h < G; ++h) {
+                        const bf16x2 pp = __builtin_bit_cast(bf16x2, row_bcast((int)pw[kb][pr], h));
+                        l[h] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l[h], false);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            acc[h][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vlo[w]),
+                                                                            acc[h][2 * w], false);
+                            acc[h][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pp, __builtin_bit_cast(bf16x2, vhi[w]),
+                                                                                acc[h][2 * w + 1], false);
+                        }
+                    }
+                }
+            continue;
+        }
         const int base = cs + r * U;
         uint4 kr[U], vr[U];
         if (CHUNK_IN_BLOCK) {
@@ -250,6 +418,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 
     if (FUSED_STORE && new_slot >= 0 && wave == 0) {
         // the new token: K/V from k_new/v_new, stored to its slot by lane group 0
+        if constexpr (kMfmaQK)
+            load_qw();
         const int64_t src = ((int64_t)s * Hkv + kvh) * D + 8 * c;
         const uint4 kn = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(a.k_new) + src);
         const uint4 vn = *reinterpret_cast<const uint4 *>(static_cast<const bf16 *>(a.v_new) + src);
@@ -428,7 +598,7 @@ hipError_t launch_decode(const DecodeArgs &a, int passes, hipStream_t stream)
     case 1: return launch_g<1, 16>(a, passes, stream);
     case 2: return launch_g<2, 16>(a, passes, stream);
     case 4: return launch_g<4, 8>(a, passes, stream);
-    case 8: return launch_g<8, 4>(a, passes, stream);
+    case 8: return launch_g<8, 8>(a, passes, stream);
     default: return hipErrorInvalidValue;
     }
 }
