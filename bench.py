@@ -22,7 +22,9 @@ The same run also measures, as sub-objects of the JSON line:
   * ``decode_head_ratios``: the 256-sequence decode at 8 Q heads over 8, 2
     and 1 KV heads (MHA, GQA, MQA: KV bytes 8:2:1);
   * ``prefill_long_chunk``: 64 new queries over 4096 keys, with and without
-    the key-split workspace.
+    the key-split workspace;
+  * ``tiny_4seq``: the 4-sequence workload (prefill round, then one decode
+    step), launch-bound: fractions of peak reported, not targeted.
 ``roofline`` is the dominant kernel of the headline step (the split-K decode
 pass with the fused store), timed alone with HIP events on its own stream;
 ``cpu_baseline`` is the fp64 CPU oracle timed on a bounded sample of the same
@@ -159,6 +161,28 @@ class DecodeSetup:
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / steps, wall
+
+    def time_batched_steps(self, n, reps, warmup):
+        """Device time per step with n steps captured in one graph (ms)."""
+        torch = self.torch
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
+                for _ in range(n):
+                    self.step_eager()
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(reps):
+            with torch.cuda.stream(self.stream):
+                g.replay()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * n)
 
     def time_kernels(self, iters):
         """Average duration of each launch (HIP events recorded on the stream the
@@ -365,6 +389,32 @@ def main():
                 f"store {t_store * 1e3:.1f} us{' (key split)' if ps.split else ''}")
             del ps
         result["prefill"] = prefill
+        # the tiny 4-sequence workload: launch-bound and cache-resident, so its fractions
+        # of peak are reported, not targeted
+        twl = workloads.make(1)
+        ts = PrefillSetup(torch, pa, twl)
+        t_store, t_attn = ts.time(max(args.steps, 10), args.warmup)
+        del ts
+        td = DecodeSetup(torch, pa, twl, args.partition)
+        td.capture()
+        t_ms, _ = td.time_steps(max(args.steps, 10), args.warmup)
+        # one replay per step is bound by the host's graph launch here; 20 steps captured
+        # in one graph give the device-side time per step
+        t_dev = td.time_batched_steps(20, max(args.steps // 10, 3), args.warmup)
+        c1_flops = prefill_flops(twl, twl.prefill)
+        result["tiny_4seq"] = {
+            "workload": "4 seqs, prompts {17, 256, 300, 511} then one decode token each, "
+                        "Hq16/Hkv8/d128, block 256, 16-block pool",
+            "prefill_ms_attention": round(float(t_attn), 5), "prefill_ms_store": round(float(t_store), 5),
+            "prefill_TFLOPs": round(c1_flops / (t_attn * 1e-3) / 1e12, 2),
+            "prefill_frac_of_mfma_peak": round(c1_flops / (t_attn * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "decode_ms_per_step": round(t_ms, 5),
+            "decode_ms_per_step_20_per_graph": round(t_dev, 5), "decode_kv_bytes": td.bytes,
+            "decode_GBs": round(td.bytes / (t_dev * 1e-3) / 1e9, 2),
+            "decode_frac_of_hbm_peak": round(td.bytes / (t_dev * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"tiny: prefill {t_attn * 1e3:.1f} us, decode step {t_ms * 1e3:.1f} us "
+            f"(one graph per step), {t_dev * 1e3:.1f} us (20 steps per graph)")
+        del td
         lwl = workloads.make(5)
         ls = DecodeSetup(torch, pa, lwl, args.partition)
         ls.capture()
