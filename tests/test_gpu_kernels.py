@@ -278,6 +278,20 @@ def test_decode_group_sizes(pa, orc, hq, hkv):
     _check(pa, orc, wl, f"decode Hq={hq} Hkv={hkv}", decode_too=True)
 
 
+@pytest.mark.parametrize("bs,part", [(1, 0), (16, 32), (64, 96), (768, 0), (256, 4096)],
+                         ids=["bs1", "bs16-p32", "bs64-p96", "bs768", "bs256-p4096"])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 1)], ids=["g4", "g8"])
+def test_decode_large_groups_paging(pa, orc, hq, hkv, bs, part):
+    """Groups of 4 and 8 Q heads (dot-product and MFMA score paths) through every
+    paging form: per-row table lookups (block sizes below 32), chunks inside one
+    block, partitions from one 32-key chunk up, ragged context tails; peaky
+    softmax and value rows that encode their position."""
+    wl = _wl(q_lens=[1] * len(CTX), k_lens=CTX, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
+             seed=27, q_scale=4.0, v_position=True)
+    _check(pa, orc, wl, f"decode Hq={hq} Hkv={hkv} bs={bs} partition={part}", decode_too=True,
+           partition_size=part)
+
+
 def test_decode_peaky_positions(pa, orc):
     wl = _wl(q_lens=[1] * 5, k_lens=[17, 513, 1025, 3000, 4096], q_scale=8.0, v_position=True,
              seed=24)
@@ -362,6 +376,15 @@ def test_decode_store_fused_groups(pa, orc, hq, hkv):
     wl = _wl(q_lens=[1] * 4, k_lens=[1, 600, 1300, 2000], num_q_heads=hq, num_kv_heads=hkv,
              seed=43, q_scale=8.0)
     _fused_case(pa, orc, wl, f"fused Hq={hq} Hkv={hkv}")
+
+
+@pytest.mark.parametrize("bs,part", [(16, 32), (256, 0)], ids=["bs16-p32", "bs256"])
+def test_decode_store_fused_mqa(pa, orc, bs, part):
+    """The fused store on the MFMA score path (8 Q heads over one KV head), with
+    per-row and per-chunk table lookups."""
+    wl = _wl(q_lens=[1] * len(CTX), k_lens=CTX, num_q_heads=8, num_kv_heads=1, block_size=bs,
+             seed=45, q_scale=4.0, v_position=True)
+    _fused_case(pa, orc, wl, f"fused MQA bs={bs} partition={part}", partition_size=part)
 
 
 def test_decode_store_fused_negative_slot_reads_pool(pa, orc):
