@@ -177,8 +177,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
         const int cs = t_begin + ch * kChunk;
         if constexpr (kMfmaQK) {
             static_assert(U == 8, "the MFMA score path takes 32-key chunks");
-            // K as the MFMA A operand: for key half kb and head-dim chunk kc, lane l holds
-            // K[key cs + 16 kb + l%16][32 kc + 8 (l/16) .. +8] (one instruction reads 16 rows
+            // K as the MFMA A operand: for key half kb and head-dim chunk q4, lane l holds
+            // K[key cs + 16 kb + l%16][32 q4 + 8 (l/16) .. +8] (one instruction reads 16 rows
             // x 64 contiguous bytes).  V in the weighting layout: lane group r owns keys
             // 4r + i and 16 + 4r + i (i < 4), the same keys the score accumulators of its
             // rows hold, so the weights move to it with row broadcasts.
