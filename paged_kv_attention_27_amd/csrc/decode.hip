@@ -52,8 +52,8 @@ __device__ __forceinline__ void dpp_add_all(float *v)
                     0, __builtin_bit_cast(int, v[i]), CTRL, 0xF, 0xF, false));
 }
 
-// value of lane h of this lane's 16-lane row (DPP row_newbcast); h is a constant
-// once the caller's loop is unrolled
+// value of lane h (0..7) of this lane's 16-lane row (DPP row_newbcast); h is a
+// constant once the caller's loop is unrolled
 __device__ __forceinline__ int row_bcast(int v, int h)
 {
     switch (h) {
