@@ -184,6 +184,21 @@ class DecodeSetup:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / (reps * n)
 
+    def time_eager_steps(self, steps, warmup):
+        """Per-step time (ms) of the same step launched directly, back to back."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step_eager()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step_eager()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     def time_kernels(self, iters):
         """Average duration of each launch (HIP events recorded on the stream the
         kernels run on): the unfused store, split-K and reduce passes, and the
@@ -348,6 +363,7 @@ def main():
     log(f"timing {args.steps} graph-replayed decode steps")
     ms_step, wall = dset.time_steps(args.steps, args.warmup)
     k_store, k_split, k_reduce, k_fused = dset.time_kernels(max(args.steps, 10))
+    ms_eager = dset.time_eager_steps(args.steps, args.warmup)
     value = dset.bytes / (ms_step * 1e-3) / 1e9
     # the fused step is a single kernel when every context fits one partition
     k_roof = k_fused if dset.n_part == 1 else k_split
@@ -365,7 +381,8 @@ def main():
                    "num_seqs": wl.num_seqs, "sum_context": int(wl.decode.seqlens_k.sum()),
                    "kv_bytes_per_step": dset.bytes, "partition_tokens":
                        args.partition or "auto", "num_partitions": dset.n_part,
-                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+                   "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+                   "ms_per_step_eager_launches": round(ms_eager, 5)},
         "roofline": {"kernel": ("decode_split_kernel with fused store" if dset.n_part == 1
                                 else "decode_split_kernel (split-K pass)"), "bound": "hbm",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
