@@ -295,8 +295,32 @@ class PrefillSetup:
         return ms.mean(axis=0)   # store, attention
 
 
+def cpu_model():
+    """The host CPU's model name (first entry of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _host_pools(orc, wl):
+    """Host copies of the pools with the workload's cached prefix stored (oracle side)."""
+    kc, vc = wl.k_cache.copy(), wl.v_cache.copy()
+    if wl.prefix is not None:
+        fx = wl.prefix
+        s = wl.extra.get("prefix_seq", None)
+        tables = wl.block_tables if s is None else np.ascontiguousarray(wl.block_tables[s:s + 1])
+        orc.store(fx.k, fx.v, orc.slot_mapping(fx.cu_seqlens_q, fx.seqlens_k, tables,
+                                               wl.block_size), kc, vc)
+    return kc, vc
+
+
 def cpu_baseline(wl, budget_s):
-    """The fp64 oracle on a bounded sample of the decode workload (first n
+    """The fp64 oracle on a bounded sample of a decode workload (first n
     sequences, new tokens stored first), in KV GB/s."""
     import oracle
     orc = oracle.get()
@@ -326,9 +350,52 @@ def cpu_baseline(wl, budget_s):
     t = run(n)
     b = decode_kv_bytes(wl, ph.seqlens_k[:n])
     return {"value": round(b / t / 1e9, 4), "unit": "GB/s", "cores": orc.num_threads(),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"fp64 decode of the first {n} of {S} sequences ({b / 1e9:.3f} GB of KV, "
-                      f"new tokens stored first), {t:.1f} s"}
+                      f"new tokens stored first), {t:.2f} s on {orc.num_threads()} threads"}
+
+
+def cpu_prefill_baseline(wl, budget_s):
+    """The fp64 oracle on a bounded sample of a prefill workload (the first n
+    sequences' attention, their keys stored first), in TFLOP/s of the same
+    algorithmic work the GPU figure counts."""
+    import oracle
+    orc = oracle.get()
+    ph = wl.prefill
+    if ph.paged:
+        kc, vc = _host_pools(orc, wl)
+        orc.store(ph.k, ph.v, orc.slot_mapping(ph.cu_seqlens_q, ph.seqlens_k, wl.block_tables,
+                                               wl.block_size), kc, vc)
+    S = len(ph.cu_seqlens_q) - 1
+    qlen = np.diff(ph.cu_seqlens_q).astype(np.int64)
+    klen = ph.seqlens_k.astype(np.int64)
+    work = 4 * wl.num_q_heads * wl.head_dim * (qlen * (klen - qlen) + qlen * (qlen + 1) // 2)
+
+    def run(n):
+        rows = int(ph.cu_seqlens_q[n])
+        q = np.ascontiguousarray(ph.q[:rows])
+        cu = np.ascontiguousarray(ph.cu_seqlens_q[:n + 1])
+        t0 = time.perf_counter()
+        if ph.paged:
+            orc.attention(q, cu, k_cache=kc, v_cache=vc,
+                          block_tables=np.ascontiguousarray(wl.block_tables[:n]),
+                          seqlens_k=np.ascontiguousarray(ph.seqlens_k[:n]), scale=wl.scale)
+        else:
+            orc.attention(q, cu, k=ph.k, v=ph.v,
+                          cu_seqlens_k=np.ascontiguousarray(ph.cu_seqlens_k[:n + 1]),
+                          scale=wl.scale)
+        return time.perf_counter() - t0
+
+    n = 1
+    rate = work[:1].sum() / max(run(1), 1e-6)
+    cum = np.cumsum(work)
+    n = S if cum[-1] / rate <= budget_s else int(max(1, np.searchsorted(cum, rate * budget_s)))
+    t = run(n)
+    f = int(cum[n - 1])
+    return {"value": round(f / t / 1e12, 6), "unit": "TFLOP/s", "cores": orc.num_threads(),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "sample": f"fp64 causal attention of the first {n} of {S} sequences "
+                      f"({f / 1e9:.2f} GFLOP), {t:.2f} s on {orc.num_threads()} threads"}
 
 
 def main():
@@ -409,6 +476,7 @@ def main():
             tflops = ps.flops / (t_attn * 1e-3) / 1e12
             prefill[pwl.name] = {
                 "value": round(tflops, 2), "unit": "TFLOP/s", "flops": ps.flops,
+                "workload": pwl.description,
                 "ms_attention": round(float(t_attn), 5), "ms_store": round(float(t_store), 5),
                 "ms_attention_all_inputs_cold": round(float(t_attn_cold), 5),
                 "key_split": ps.split,
@@ -420,7 +488,19 @@ def main():
                 f"({t_attn_cold * 1e3:.1f} us with every input cold), "
                 f"store {t_store * 1e3:.1f} us{' (key split)' if ps.split else ''}")
             del ps
-        result["prefill"] = prefill
+            if not args.no_cpu_baseline:
+                log(f"timing the CPU oracle on {pwl.name}")
+                prefill[pwl.name]["cpu_baseline"] = cpu_prefill_baseline(pwl, args.cpu_budget)
+        # the prefill half of the metric, headed by the throughput-bound prefix-cache batch
+        # (16 sequences over a shared 512-token prefix); the no-cache batch beside it
+        head = prefill["c3_prefix_chunked_prefill"]
+        result["prefill"] = {
+            "value": head["value"], "unit": "TFLOP/s",
+            "config": {"workload": head["workload"], "flops": head["flops"]},
+            "ms_attention": head["ms_attention"],
+            "roofline": head["roofline"],
+            **({"cpu_baseline": head["cpu_baseline"]} if "cpu_baseline" in head else {}),
+            "configs": prefill}
         # the tiny 4-sequence workload: launch-bound and cache-resident, so its fractions
         # of peak are reported, not targeted
         twl = workloads.make(1)
@@ -459,7 +539,11 @@ def main():
             "split_GBs": round(ls.bytes / (l_split * 1e-3) / 1e9, 2),
             "ms_split": round(float(l_split), 5), "ms_reduce": round(float(l_reduce), 5)}
         log(f"long decode: {l_ms * 1e3:.1f} us/step, split {l_split * 1e3:.1f} us")
-        del ls, lwl
+        del ls
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on the long decode")
+            result["decode_long"]["cpu_baseline"] = cpu_baseline(lwl, args.cpu_budget)
+        del lwl
         torch.cuda.empty_cache()
 
         # MHA / GQA / MQA at 8 Q heads: KV bytes 8:2:1 for the same lengths

@@ -184,8 +184,9 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t
  * the second to finish merges the two partial softmax states, rescaling both
  * to the larger running maximum (the log-sum-exp combination that lets the
  * blocked computation of [Atlas] ch.22 avoid the full score matrix).  Results
- * differ from pa_prefill_varlen only by rounding (the partials are stored as
- * fp16 O / l with fp32 max and sum).
+ * differ from pa_prefill_varlen only by fp32 rounding (each half's partial
+ * O / l, running max and sum are stored in fp32, so every bf16 value range is
+ * covered).
  *
  * workspace  (device) >= pa_prefill_workspace_size(...) bytes (sized on the
  *            device the call runs on), 16-byte aligned, zero-filled before its

@@ -111,9 +111,9 @@ struct PrefillArgs {
     void *ws_part;      // [items][2] partials of kPrefillPartBytes each
     int32_t *ws_cnt;    // [items] arrival counters; zero between calls
 };
-// bytes of one half's partial: O / l as fp16 pairs [4 waves][32][64 lanes] u32, then the
-// column max and sum as fp32 [4 waves][2][64 lanes]
-constexpr size_t kPrefillPartBytes = (4 * 32 * 64 + 4 * 2 * 64) * 4;
+// bytes of one half's partial: O / l as fp32 [4 waves][64][64 lanes], then the column max
+// and sum as fp32 [4 waves][2][64 lanes]
+constexpr size_t kPrefillPartBytes = (4 * 64 * 64 + 4 * 2 * 64) * 4;
 constexpr int kPrefillMinSplitTiles = 4;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // items of a batch of these sizes that key-split mode would cover on the current

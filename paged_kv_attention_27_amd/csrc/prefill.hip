@@ -99,7 +99,7 @@ __device__ __forceinline__ float other_half(float x, int hl) {
 // follow each other on the same stages.  half = -1: the whole key range, output
 // written here.  half = 0 / 1 (key-split mode): an item with at least
 // kPrefillMinSplitTiles key tiles is split at tile n/2; this call computes one half,
-// stores its partial (O / l in fp16, column max and sum in fp32), and the second of
+// stores its partial (O / l, column max and sum, all fp32), and the second of
 // the two workgroups to finish merges both (log-sum-exp combination: rescale each
 // to the larger maximum) and writes the output.  A smaller item is done whole by
 // half 0; half 1 returns.
@@ -347,7 +347,7 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         const int n_lvl = (a.max_seqlen_q + BM - 1) / BM;
         const int64_t item = ((int64_t)s * n_lvl + qb) * Hkv + kvh;
         constexpr int kWords = (int)(kPrefillPartBytes / 4);
-        constexpr int kOWords = 4 * 32 * 64;
+        constexpr int kOWords = 4 * 64 * 64;
         uint32_t *mine = static_cast<uint32_t *>(a.ws_part) + (item * 2 + half) * kWords;
         const float inv = l > 0.f ? 1.f / l : 0.f;   // a column may see no key of this half
         // The partial and the counter use device-scope (coherent across XCDs) relaxed
@@ -365,10 +365,8 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
 #pragma unroll
         for (int mtd = 0; mtd < 4; ++mtd)
 #pragma unroll
-            for (int v2 = 0; v2 < 8; ++v2) {
-                const auto h2 = __builtin_amdgcn_cvt_pkrtz(acc_o[mtd][2 * v2] * inv, acc_o[mtd][2 * v2 + 1] * inv);
-                st(mine + (wave * 32 + 8 * mtd + v2) * 64 + lane, __builtin_bit_cast(uint32_t, h2));
-            }
+            for (int v = 0; v < 16; ++v)
+                st(mine + (wave * 64 + 16 * mtd + v) * 64 + lane, __float_as_uint(acc_o[mtd][v] * inv));
         st(mine + kOWords + (wave * 2 + 0) * 64 + lane, __float_as_uint(m));
         st(mine + kOWords + (wave * 2 + 1) * 64 + lane, __float_as_uint(l));
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's stores are complete
@@ -380,6 +378,10 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
         __syncthreads();                      // *arrival is read by all before its next use
         if (!second)
             return;
+        // the partner's partial is read only after its arrival was seen: no load below may
+        // be moved above this point (the branch already orders them in the hardware, which
+        // issues a wave's instructions in order)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
         const uint32_t *other = static_cast<const uint32_t *>(a.ws_part) + (item * 2 + (1 - half)) * kWords;
         const float m1 = __uint_as_float(ldc(other + kOWords + (wave * 2 + 0) * 64 + lane));
         const float l1 = __uint_as_float(ldc(other + kOWords + (wave * 2 + 1) * 64 + lane));
@@ -398,12 +400,9 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
                     const int d0 = 32 * mtd + 8 * g4 + 4 * hl;
                     float o[4];
 #pragma unroll
-                    for (int e2 = 0; e2 < 2; ++e2) {
-                        const uint32_t w = ldc(other + (wave * 32 + 8 * mtd + 2 * g4 + e2) * 64 + lane);
-                        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-                        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-                        o[2 * e2] = (acc_o[mtd][4 * g4 + 2 * e2] * w0 + lo * w1) * inv2;
-                        o[2 * e2 + 1] = (acc_o[mtd][4 * g4 + 2 * e2 + 1] * w0 + hi * w1) * inv2;
+                    for (int e = 0; e < 4; ++e) {
+                        const float w = __uint_as_float(ldc(other + (wave * 64 + 16 * mtd + 4 * g4 + e) * 64 + lane));
+                        o[e] = (acc_o[mtd][4 * g4 + e] * w0 + w * w1) * inv2;
                     }
                     uint2 pk;
                     pk.x = pack_bf16x2(o[0], o[1]);

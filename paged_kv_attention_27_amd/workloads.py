@@ -309,7 +309,7 @@ def make(cfg_id: int, values: bool = True) -> Workload:
 
 def synthetic(q_lens, k_lens, num_q_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
               seed=0, paged=True, q_scale=1.0, q_zero=False, v_position=False,
-              extra_blocks=3, name="synthetic") -> Workload:
+              v_scale=1.0, extra_blocks=3, name="synthetic") -> Workload:
     """A small seeded problem with discriminating options for parity tests.
 
     Sequence s has k_lens[s] tokens of which the last q_lens[s] are new.  With
@@ -318,7 +318,8 @@ def synthetic(q_lens, k_lens, num_q_heads=16, num_kv_heads=8, head_dim=128, bloc
     q_lens must equal k_lens and attention reads the flat k/v.
     Options: ``q_scale`` multiplies q (8 gives a peaky softmax), ``q_zero``
     makes every weight equal, ``v_position`` writes each value row's position
-    into its first two elements as (j mod 16)/16 and ((j div 16) mod 16)/16.
+    into its first two elements as (j mod 16)/16 and ((j div 16) mod 16)/16,
+    ``v_scale`` multiplies every value row (outputs then scale with it).
     """
     meta, _, r_pre, r_fix, _ = _streams(seed)
     q_lens = np.asarray(q_lens, dtype=np.int64)
@@ -349,6 +350,10 @@ def synthetic(q_lens, k_lens, num_q_heads=16, num_kv_heads=8, head_dim=128, bloc
                 j = first[s] + np.arange(b - a)
                 ph.v[a:b, :, 0] = f32_to_bf16_bits(((j % 16) / 16.0).astype(np.float32))[:, None]
                 ph.v[a:b, :, 1] = f32_to_bf16_bits((((j // 16) % 16) / 16.0).astype(np.float32))[:, None]
+    if v_scale != 1.0:
+        for ph in (prefix, prefill):
+            if ph is not None:
+                ph.v[:] = f32_to_bf16_bits(bf16_bits_to_f32(ph.v) * np.float32(v_scale))
     wl = Workload(name, "synthetic parity problem", Hq, Hkv, d, bs, NB, _scale(d), bt,
                   _nan_pool(NB, bs, Hkv, d), _nan_pool(NB, bs, Hkv, d), prefix=prefix,
                   prefill=prefill)

@@ -15,6 +15,9 @@ import torch
 
 PARITY_MAX = 2e-2    # max |gpu - oracle| on bf16 outputs (spec tolerance)
 PARITY_MEAN = 2e-3   # mean |gpu - oracle|
+# bytes of one half's partial in the prefill key-split workspace (include/pa.h): fp32 O / l
+# [4 waves][64][64 lanes], then fp32 max and sum [4 waves][2][64 lanes]
+PREFILL_PART_BYTES = (4 * 64 * 64 + 4 * 2 * 64) * 4
 
 
 def log(msg):

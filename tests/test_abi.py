@@ -113,7 +113,7 @@ def test_prefill_validation(lib):
     assert _prefill(lib, mq=0, q=None) == OK
 
 
-PART_BYTES = (4 * 32 * 64 + 4 * 2 * 64) * 4
+PART_BYTES = (4 * 64 * 64 + 4 * 2 * 64) * 4   # fp32 O / l, then max and sum
 
 
 def test_prefill_workspace_size(lib):

@@ -11,7 +11,8 @@ import numpy as np
 import pytest
 import torch
 
-from pipelines import check_close, dev_bf16, dev_i32, host_f64, host_u16, log, prefix_tables
+from pipelines import (PREFILL_PART_BYTES, check_close, dev_bf16, dev_i32, host_f64, host_u16, log,
+                       prefix_tables)
 
 pytestmark = pytest.mark.gpu
 
@@ -197,7 +198,7 @@ def test_prefill_graph_replays(orc, split):
         got = host_f64(out_s)
         if split:
             assert int(ws.count_nonzero()) > 0                    # the partials are there ...
-            n_items = ws.numel() // (2 * (4 * 32 * 64 + 4 * 2 * 64) * 4 + 4)
+            n_items = ws.numel() // (2 * PREFILL_PART_BYTES + 4)
             tail = ws[ws.numel() - 4 * n_items:]
             assert int(tail.count_nonzero()) == 0, "arrival counters not reset"   # ... not the counts
         eager = pa.pa_prefill_varlen(dev_bf16(q), None, None, kc, vc, bt, cu_q, cu_k,

@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from pipelines import (check_close, cu_of, dev_bf16, dev_i32, host_f64, host_u16, log,
-                       oracle_pipeline, prefix_tables)
+from pipelines import (PREFILL_PART_BYTES, check_close, cu_of, dev_bf16, dev_i32, host_f64,
+                       host_u16, log, oracle_pipeline, prefix_tables)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -201,7 +201,7 @@ def test_prefill_many_query_blocks(pa, orc, hq, hkv, bs, paged):
     _check(pa, orc, wl, f"many blocks Hq={hq} Hkv={hkv} bs={bs} paged={paged}")
 
 
-PART_BYTES = (4 * 32 * 64 + 4 * 2 * 64) * 4   # one half's partial in the prefill workspace
+PART_BYTES = PREFILL_PART_BYTES   # one half's partial in the prefill workspace
 
 
 SPLIT_CASES = {   # (hq, hkv, block size, paged, peaky, q_lens, k_lens): few, long query blocks
@@ -237,6 +237,34 @@ def test_prefill_key_split(pa, orc, case):
     # the unsplit path on the same inputs agrees to the same tolerance
     g0 = _gpu_synthetic(pa, wl)
     check_close(g0["prefill"], o["prefill"], label + " unsplit")
+
+
+@pytest.mark.parametrize("v_scale", [1e5, 1e30, 1e-6])
+def test_prefill_key_split_value_range(pa, orc, v_scale):
+    """The key split stores each half's partial O / l in fp32, so it covers the
+    whole range of bf16 values: with |V| around 1e5, 1e30 and 1e-6 (outside
+    fp16's range, or in its subnormals) the split result stays finite, matches
+    the unsplit call to a relative 2^-7 of the value scale, and matches the
+    oracle to the usual tolerance after dividing by that scale (the log-sum-exp
+    merge of partial softmax states, "Visual atlas" ch.22 captions)."""
+    hq, hkv = 16, 8
+    q, k = [64, 200], [4096, 2600]
+    wl = _wl(q_lens=q, k_lens=k, num_q_heads=hq, num_kv_heads=hkv, block_size=256,
+             v_scale=v_scale, seed=31)
+    ph = wl.prefill
+    assert pa.pa_prefill_workspace_size(len(q), ph.max_seqlen_q, ph.max_seqlen_k, hq, hkv) > 0
+    ws = pa.pa_prefill_workspace(len(q), ph.max_seqlen_q, ph.max_seqlen_k, hq, hkv)
+    label = f"key split |V| ~ {v_scale:g}"
+    log(f"[{label}]")
+    gs = _gpu_synthetic(pa, wl, workspace=ws)
+    g0 = _gpu_synthetic(pa, wl)
+    o = oracle_pipeline(orc, wl)
+    assert np.isfinite(gs["prefill"]).all() and np.isfinite(g0["prefill"]).all()
+    rel = np.abs(gs["prefill"] - g0["prefill"]).max() / v_scale
+    log(f"  split vs unsplit: max |diff| / scale = {rel:.3e}")
+    assert rel <= 2.0 ** -7
+    check_close(gs["prefill"] / v_scale, o["prefill"] / v_scale, label)
+    check_close(g0["prefill"] / v_scale, o["prefill"] / v_scale, label + " unsplit")
 
 
 def test_prefill_workspace_errors(pa):
