@@ -59,7 +59,9 @@ typedef enum {
                                inconsistent with each other                      */
     PA_ERR_UNSUPPORTED = 3, /* valid sizes this build has no kernel for           */
     PA_ERR_WORKSPACE = 4,   /* workspace_bytes smaller than required              */
-    PA_ERR_LAUNCH = 5       /* the HIP runtime reported a launch error            */
+    PA_ERR_LAUNCH = 5,      /* the HIP runtime reported a launch error            */
+    PA_ERR_SCRATCH = 6      /* the call needs more than the library's fixed device
+                               scratch (pa_decode_noalloc)                       */
 } pa_status;
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -304,6 +306,32 @@ int pa_decode_reduce(const void *q, const void *k_cache, const void *v_cache,
                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                      int32_t block_size, float scale, int32_t partition_size,
                      void *workspace, size_t workspace_bytes, void *out, hipStream_t stream);
+
+/*
+ * pa_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same operation, arguments (minus workspace) and
+ * results as pa_decode: the partials of a split context go to a fixed device
+ * array inside the library, PA_NOALLOC_SCRATCH_BYTES on each device, held
+ * until the process ends.  The call allocates nothing; its first call on a
+ * device looks up that device's copy of the array.
+ *
+ * Returns PA_ERR_SCRATCH, launching nothing, when
+ * pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+ * max_context_len, partition_size) exceeds PA_NOALLOC_SCRATCH_BYTES (for
+ * example 16 sequences x 32 Q heads x 32768 keys need 8.5 MB at the default
+ * partition size).  Every call on one device shares that device's array:
+ * calls that may overlap in time on one device (other streams, other host
+ * threads) race and must not be issued; calls on one stream are ordered.
+ * Nothing in the array needs to start at zero.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int pa_decode_noalloc(const void *q, const void *k_cache, const void *v_cache,
+                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                      const int32_t *context_lens, int32_t num_seqs, int32_t max_context_len,
+                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, float scale, int32_t partition_size, void *out,
+                      hipStream_t stream);
 
 /*
  * Host block manager with prefix caching.

@@ -12,7 +12,8 @@ from .binding import (PaError, library_path, load, pa_decode, pa_decode_workspac
                       pa_decode_num_partitions, pa_decode_split, pa_decode_reduce,
                       pa_decode_store, BlockManager, pa_bm_create, pa_bm_destroy,
                       pa_bm_num_free, pa_bm_ref_count, pa_bm_blocks_needed, pa_bm_allocate,
-                      pa_bm_append, pa_bm_free, pa_kv_pool_layout, alloc_kv_pools)
+                      pa_bm_append, pa_bm_free, pa_kv_pool_layout, alloc_kv_pools,
+                      pa_decode_noalloc, NOALLOC_SCRATCH_BYTES)
 
 __all__ = ["PaError", "library_path", "load", "pa_store_kv", "pa_prefill_varlen",
            "pa_prefill_workspace_size", "pa_prefill_workspace", "pa_decode",
@@ -20,4 +21,5 @@ __all__ = ["PaError", "library_path", "load", "pa_store_kv", "pa_prefill_varlen"
            "pa_decode_reduce", "pa_decode_store", "pa_slot_mapping",
            "pa_status_string", "BlockManager", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_blocks_needed", "pa_bm_allocate",
-           "pa_bm_append", "pa_bm_free", "pa_kv_pool_layout", "alloc_kv_pools"]
+           "pa_bm_append", "pa_bm_free", "pa_kv_pool_layout", "alloc_kv_pools",
+           "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES"]

@@ -66,6 +66,9 @@ def load():
         fn.restype = ctypes.c_int
         fn.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float,
                        _I, _P, _SZ, _P, _P]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I,
+                                      ctypes.c_float, _I, _P, _P]
     lib.pa_decode_store.restype = ctypes.c_int
     lib.pa_decode_store.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                     _I, ctypes.c_float, _I, _P, _SZ, _P, _P]
@@ -244,6 +247,26 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, max_context_len, 
         bs, float(scale), int(partition_size), _dev(workspace, torch.uint8, "workspace"),
         workspace.numel(), _dev(out, torch.bfloat16, "out"), _stream(stream))
     _check(_entry, st)
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # PA_NOALLOC_SCRATCH_BYTES in include/pa.h
+
+
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                      out, partition_size=0, stream=None):
+    """pa_decode with the partials in the library's fixed device scratch: no workspace
+    argument and nothing allocated by the call (``out`` is the caller's)."""
+    S, Hq, d = q.shape
+    NB, bs, Hkv, _ = k_cache.shape
+    st = load().pa_decode_noalloc(
+        _dev(q, torch.bfloat16, "q"), _dev(k_cache, torch.bfloat16, "k_cache"),
+        _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, torch.int32, "context_lens"), S, int(max_context_len), Hq, Hkv, d,
+        bs, float(scale), int(partition_size), _dev(out, torch.bfloat16, "out"),
+        _stream(stream))
+    _check("pa_decode_noalloc", st)
     return out
 
 

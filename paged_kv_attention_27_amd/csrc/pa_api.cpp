@@ -76,6 +76,7 @@ const char *pa_status_string(int status)
     case PA_ERR_UNSUPPORTED: return "sizes are valid but not supported by this build";
     case PA_ERR_WORKSPACE: return "workspace is too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
+    case PA_ERR_SCRATCH: return "the call needs more than the library's fixed device scratch";
     default: return "unknown status";
     }
 }

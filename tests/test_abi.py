@@ -51,7 +51,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(6):
+    for code in range(7):
         assert lib.pa_status_string(code)
     assert b"unknown" in lib.pa_status_string(99)
 
