@@ -23,7 +23,11 @@ _SZ = ctypes.c_size_t
 
 class PaError(RuntimeError):
     def __init__(self, fn: str, status: int):
-        super().__init__(f"{fn} failed: {pa_status_string(status)} (status {status})")
+        try:
+            what = pa_status_string(status)
+        except (OSError, RuntimeError):   # e.g. only the block manager is loaded
+            what = "error"
+        super().__init__(f"{fn} failed: {what} (status {status})")
         self.status = status
 
 
@@ -72,6 +76,12 @@ def load():
     lib.pa_decode_store.restype = ctypes.c_int
     lib.pa_decode_store.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                     _I, ctypes.c_float, _I, _P, _SZ, _P, _P]
+    _bind_block_manager(lib)
+    _LIB = lib
+    return lib
+
+
+def _bind_block_manager(lib):
     _U64 = ctypes.c_uint64
     lib.pa_bm_create.restype = _P
     lib.pa_bm_create.argtypes = [_I, _I]
@@ -89,8 +99,25 @@ def load():
     lib.pa_bm_append.argtypes = [_P, _P, _I, _U64, _P, _I]
     lib.pa_bm_free.restype = ctypes.c_int
     lib.pa_bm_free.argtypes = [_P, _P, _I]
-    _LIB = lib
-    return lib
+
+
+_BM_LIB = None
+
+
+def _bm():
+    """The library the host block manager (pa_bm_*) is called in: libpa.so, or, when
+    PA_BM_LIBRARY names one, a separate build of block_manager.cpp (say, one built
+    with a sanitizer); either way the same C code behind the same declarations."""
+    global _BM_LIB
+    if _BM_LIB is None:
+        path = os.environ.get("PA_BM_LIBRARY")
+        if path:
+            lib = ctypes.CDLL(path)
+            _bind_block_manager(lib)
+            _BM_LIB = lib
+        else:
+            _BM_LIB = load()
+    return _BM_LIB
 
 
 def pa_status_string(status: int) -> str:
@@ -321,27 +348,27 @@ def _host_i32(x):
 
 
 def pa_bm_create(num_blocks, block_size):
-    h = load().pa_bm_create(int(num_blocks), int(block_size))
+    h = _bm().pa_bm_create(int(num_blocks), int(block_size))
     if not h:
         raise ValueError(f"pa_bm_create({num_blocks}, {block_size}) failed")
     return h
 
 
 def pa_bm_destroy(bm):
-    load().pa_bm_destroy(bm)
+    _bm().pa_bm_destroy(bm)
 
 
 def pa_bm_num_free(bm):
-    return load().pa_bm_num_free(bm)
+    return _bm().pa_bm_num_free(bm)
 
 
 def pa_bm_ref_count(bm, block):
-    return load().pa_bm_ref_count(bm, int(block))
+    return _bm().pa_bm_ref_count(bm, int(block))
 
 
 def pa_bm_blocks_needed(bm, tokens, salt=0):
     t = _host_i32(tokens)
-    return load().pa_bm_blocks_needed(bm, t.data_ptr(), t.numel(), int(salt))
+    return _bm().pa_bm_blocks_needed(bm, t.data_ptr(), t.numel(), int(salt))
 
 
 def pa_bm_allocate(bm, tokens, max_blocks, salt=0):
@@ -349,7 +376,7 @@ def pa_bm_allocate(bm, tokens, max_blocks, salt=0):
     t = _host_i32(tokens)
     table = torch.empty(int(max_blocks), dtype=torch.int32)
     cached = ctypes.c_int32(0)
-    _check("pa_bm_allocate", load().pa_bm_allocate(bm, t.data_ptr(), t.numel(), int(salt),
+    _check("pa_bm_allocate", _bm().pa_bm_allocate(bm, t.data_ptr(), t.numel(), int(salt),
                                                    table.data_ptr(), table.numel(),
                                                    ctypes.byref(cached)))
     return table, cached.value
@@ -361,13 +388,13 @@ def pa_bm_append(bm, tokens, block_table, salt=0):
     if block_table.dtype != torch.int32 or block_table.device.type != "cpu" \
             or not block_table.is_contiguous():
         raise TypeError("block_table: expected a contiguous int32 CPU tensor")
-    _check("pa_bm_append", load().pa_bm_append(bm, t.data_ptr(), t.numel(), int(salt),
+    _check("pa_bm_append", _bm().pa_bm_append(bm, t.data_ptr(), t.numel(), int(salt),
                                                block_table.data_ptr(), block_table.numel()))
 
 
 def pa_bm_free(bm, block_table):
     bt = _host_i32(block_table)
-    _check("pa_bm_free", load().pa_bm_free(bm, bt.data_ptr(), bt.numel()))
+    _check("pa_bm_free", _bm().pa_bm_free(bm, bt.data_ptr(), bt.numel()))
 
 
 class BlockManager:
