@@ -246,10 +246,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * workspace     (device) >= pa_decode_workspace_size(...) bytes, any content
  * out           (device, out) [num_seqs, num_q_heads, head_dim] bf16
  * partition_size  0 (library's choice: one partition per sequence when
- *               num_seqs * num_kv_heads >= 512, else a multiple of 256 keys, at
- *               least 1024, that makes num_seqs * num_kv_heads * partitions
- *               about 4096) or a multiple of 32 tokens
- * Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8}.
+ *               num_seqs * num_kv_heads >= 1024; otherwise partitions of at most
+ *               2048 keys that shrink toward the end of each sequence: counted
+ *               from the end of the context rounded up to 64, 256, 256, 512, 512,
+ *               1024, 1024, then 2048 keys, the first partition taking the rest)
+ *               or a multiple of 32: fixed partitions of that many keys
+ * Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
+ * num_seqs <= 65535 and at most 65535 partitions (max_context_len /
+ * partition_size rounded up), else PA_ERR_UNSUPPORTED.
  */
 int pa_decode(const void *q, const void *k_cache, const void *v_cache,
               const int32_t *block_tables, int32_t max_blocks_per_seq,

@@ -12,9 +12,10 @@
 namespace {
 
 constexpr int kHeadDim = 128;
-constexpr int64_t kDecodeTargetWorkgroups = 4096;   // ~16 per CU on 256 CUs
-constexpr int64_t kDecodeWholeSequencePairs = 512;   // (sequence, KV head) pairs that fill the chip
-constexpr int64_t kDecodeMinPartition = 1024;        // keys: below this, per-workgroup overhead dominates
+// library decode partitioning (partition_size == 0); see resolve_partition
+constexpr int64_t kDecodeWholeSequencePairs = 1024;   // (sequence, KV head) pairs that fill the chip
+constexpr int32_t kDecodePartMax = 2048;              // keys: the largest partition
+constexpr int32_t kDecodePartMin = 256;               // keys: the last partition of a sequence
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -33,34 +34,33 @@ bool group_supported(int32_t hq, int32_t hkv) {
     return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
-// Library's decode partition size (host integers only), tuned on MI355X.
-// With at least 512 (sequence, KV head) pairs every sequence is one
-// partition: the grid already fills the chip, and whole-sequence workgroups
-// need no partials or merge.  Otherwise the context is split so the grid
-// holds about 4096 workgroups, but never into partitions under 1024 keys,
-// where each workgroup's fixed cost (query load, four-wave merge, partial
-// write) outweighs its streaming time.  Multiples of 256 keys.
-int32_t resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
-                          int32_t max_context_len) {
+struct Plan {
+    int32_t P, u;   // pa::plan_count / plan_range parameters
+};
+
+// Decode partitioning (host integers only, tuned on MI355X).  An explicit
+// partition_size gives fixed partitions of that many keys.  Otherwise, with at
+// least 1024 (sequence, KV head) pairs every sequence is one partition: the grid
+// already fills the chip several times over, and whole-sequence workgroups need no
+// partials or merge pass.  With fewer pairs the keys are split into partitions of
+// at most 2048 keys that shrink to 256 toward the end of each sequence, so the
+// workgroups launched last are short and the chip drains evenly (measured on
+// MI355X against fixed 1024-key partitions: 16 x 32768 keys at Hkv 8 354 -> 343 us,
+// 256 ragged contexts at Hq 8 / Hkv 1 78 -> 65 us).
+Plan resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
+                       int32_t max_context_len) {
     if (partition_size != 0)
-        return partition_size;
+        return {partition_size, 0};
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-    int64_t part = max_context_len;
-    if (pairs > 0 && pairs < kDecodeWholeSequencePairs) {
-        part = ((int64_t)max_context_len * pairs + kDecodeTargetWorkgroups - 1) / kDecodeTargetWorkgroups;
-        if (part < kDecodeMinPartition)
-            part = kDecodeMinPartition;
+    if (pairs >= kDecodeWholeSequencePairs) {
+        const int64_t whole = ((int64_t)max_context_len + 255) / 256 * 256;
+        return {(int32_t)(whole < 256 ? 256 : whole > (1 << 30) ? (1 << 30) : whole), 0};
     }
-    part = (part + 255) / 256 * 256;
-    if (part < 256)
-        part = 256;
-    return (int32_t)(part > (1 << 30) ? (1 << 30) : part);
+    return {kDecodePartMax, kDecodePartMin};
 }
 
-int32_t num_partitions(int32_t max_context_len, int32_t part) {
-    if (max_context_len <= 0)
-        return 1;   // one (empty) partition: the reduce pass writes the zero rows
-    return (int32_t)(((int64_t)max_context_len + part - 1) / part);
+int32_t num_partitions(int32_t max_context_len, Plan pl) {
+    return pa::plan_count(max_context_len, pl.P, pl.u);
 }
 
 }  // namespace
@@ -322,8 +322,10 @@ int decode_passes(const void *q, const void *k_cache, const void *v_cache,
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0)
         return PA_OK;
-    const int32_t part = resolve_partition(partition_size, num_seqs, num_kv_heads,
-                                           max_context_len);
+    const Plan part = resolve_partition(partition_size, num_seqs, num_kv_heads,
+                                        max_context_len);
+    if (num_partitions(max_context_len, part) > 65535)
+        return PA_ERR_UNSUPPORTED;   // partitions are a grid dimension
     if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
         return PA_ERR_NULL;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
@@ -356,7 +358,12 @@ int decode_passes(const void *q, const void *k_cache, const void *v_cache,
     a.num_kv_heads = num_kv_heads;
     a.block_size = block_size;
     a.bs_shift = log2_if_pow2(block_size);
-    a.part_tokens = part;
+    a.part_tokens = part.P;
+    a.part_min = part.u;
+    // row z of the grid holds sequence (y + seq_rot z) mod S at position y; with
+    // S - seq_rot odd, a sequence moves by an odd multiple of Hkv positions modulo 8
+    // (its XCD) from one partition row to the next
+    a.seq_rot = (num_seqs % 2 == 0) ? 1 : 2;
     a.scale_log2 = scale * pa::kLog2e;
     hipError_t e = pa::launch_decode(a, passes, stream);
     return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH;

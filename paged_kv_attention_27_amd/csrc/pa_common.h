@@ -77,10 +77,75 @@ struct DecodeArgs {
     int32_t num_kv_heads;
     int32_t block_size;
     int32_t bs_shift;   // log2(block_size) if a power of two, else -1
-    int32_t part_tokens;
-    int32_t n_part;
+    int32_t part_tokens;   // P: the largest partition (see plan_count)
+    int32_t part_min;      // 0: fixed partitions; else the smallest tail partition
+    int32_t n_part;        // plan_count(max_context_len): grid depth and partial slots
+    int32_t seq_rot;       // grid-to-sequence rotation per partition row (XCD balance)
     float scale_log2;   // scale * log2(e)
 };
+
+// ------------------------------------------------ decode partition plan
+// How the n keys of one sequence are split into partitions, each reduced to one
+// partial by one workgroup.
+//  * part_min == 0: fixed partitions [p P, (p + 1) P), ceil(n / P) of them.
+//  * part_min = u > 0 (u a multiple of 64, P = u 2^k, k >= 1): partitions shrink
+//    toward the end of the key range.  Counted from the end of n64 = n rounded
+//    up to 64, their sizes are u, u, 2u, 2u, ..., P/2, P/2 (the tail, 2 (P - u)
+//    keys), then P up to the start, where the first partition takes what is
+//    left.  A grid of fixed-size partitions ends with a wave of full-size
+//    workgroups that run nearly alone; here the last workgroups launched are small.
+// Every boundary of the second kind is a multiple of 64 keys; a sequence with
+// n <= 0 has one (empty) partition.
+__host__ __device__ inline int32_t plan_tail_size(int32_t j, int32_t u) { return u << (j >> 1); }
+
+__host__ __device__ inline int32_t plan_count(int32_t n, int32_t P, int32_t u)
+{
+    if (n <= 0)
+        return 1;
+    if (u == 0)
+        return (int32_t)(((int64_t)n + P - 1) / P);
+    const int64_t n64 = ((int64_t)n + 63) / 64 * 64;
+    const int64_t T = 2 * ((int64_t)P - u);
+    if (n64 > T) {
+        int32_t nt = 0;
+        for (int32_t v = u; v < P; v *= 2) nt += 2;
+        return (int32_t)((n64 - T + P - 1) / P) + nt;
+    }
+    int64_t c = 0;
+    int32_t m = 0;
+    while (c < n64) c += plan_tail_size(m++, u);
+    return m;
+}
+
+// keys [b, e) of partition p (0 <= p < plan_count) of a sequence of n > 0 keys
+__host__ __device__ inline void plan_range(int32_t p, int32_t n, int32_t P, int32_t u, int32_t &b,
+                                           int32_t &e)
+{
+    if (u == 0) {
+        b = p * P;
+        e = (int32_t)((int64_t)b + P < n ? b + P : n);
+        return;
+    }
+    const int64_t n64 = ((int64_t)n + 63) / 64 * 64;
+    const int64_t T = 2 * ((int64_t)P - u);
+    const int32_t cnt = plan_count(n, P, u);
+    int64_t ee, bb;
+    int32_t nt = 0;
+    for (int32_t v = u; v < P; v *= 2) nt += 2;
+    const int32_t nh = n64 > T ? cnt - nt : 0;   // full-size partitions ahead of the tail
+    if (p < nh) {
+        ee = n64 - T - (int64_t)(nh - 1 - p) * P;
+        bb = ee - P;
+    } else {
+        const int32_t j = cnt - 1 - p;             // tail index, 0 = the last partition
+        int64_t c = 0;
+        for (int32_t i = 0; i < j; ++i) c += plan_tail_size(i, u);
+        ee = n64 - c;
+        bb = ee - plan_tail_size(j, u);
+    }
+    b = (int32_t)(bb > 0 ? bb : 0);
+    e = (int32_t)(ee < n ? ee : n);
+}
 // passes: bit 0 = partition (split) pass, bit 1 = reduce pass
 hipError_t launch_decode(const DecodeArgs &a, int passes, hipStream_t stream);
 

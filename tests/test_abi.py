@@ -176,6 +176,9 @@ def test_decode_validation(lib):
     assert _decode(lib, scale=-1.0) == SHAPE
     assert _decode(lib, q=None) == NULL
     assert _decode(lib, S=0, q=None) == OK
+    # partitions are a grid dimension: 65535 at most, checked before the workspace
+    assert _decode(lib, maxb=65536, mctx=65535 * 32, part=32, wsb=0) == WORKSPACE
+    assert _decode(lib, maxb=65536, mctx=65535 * 32 + 1, part=32, wsb=0) == UNSUPPORTED
 
 
 def test_decode_store_validation(lib):
@@ -203,12 +206,32 @@ def test_decode_sizes(lib):
     assert np_(4, 8, 100, 33) == 0
     assert lib.pa_decode_workspace_size(3, 16, 8, 128, 1000, 256) == 3 * 16 * 4 * 130 * 4
     assert np_(256, 8, 4096, 0) == 1      # auto: 2048 pairs fill the chip, one partition
-    assert np_(256, 2, 4096, 0) == 1      # auto: 512 pairs, one partition
-    assert np_(256, 1, 4096, 0) == 4      # auto: 256 pairs, 1024-key partitions
-    assert np_(16, 8, 32768, 0) == 32     # auto: 1024-key partitions, 4096 workgroups
-    assert np_(4, 8, 512, 0) == 1         # auto: at least 1024 keys
-    assert np_(1, 8, 10**6, 0) == 489     # auto: 1954 keys, rounded up to 2048
-    assert np_(1, 1, 3000, 0) == 3        # auto: 1024-key minimum
+    assert np_(256, 4, 4096, 0) == 1      # auto: 1024 pairs, one partition
+    # auto, fewer pairs: partitions of 2048 keys shrinking to 256 at the end of each
+    # sequence (from the end: 256, 256, 512, 512, 1024, 1024, then 2048s)
+    assert np_(256, 2, 4096, 0) == 7      # 4096 = 512 + 3584
+    assert np_(256, 1, 4096, 0) == 7
+    assert np_(16, 8, 32768, 0) == 21     # 15 partitions up to the 3584-key tail, then 6
+    assert np_(4, 8, 1024, 0) == 3        # 1024 = 512 + 256 + 256
+    assert np_(4, 8, 100, 0) == 1         # rounded up to 128: one partition
+    assert np_(1, 1, 3000, 0) == 6        # 3008 (rounded to 64) = 448 + 2560
+    assert np_(1, 8, 10**6, 0) == 493
+    for n in list(range(0, 9000, 7)) + [10**5 + 3, 2**20]:
+        assert np_(1, 1, n, 0) == _shrinking_count(n, 2048, 256), n
+
+
+def _shrinking_count(n, big, small):
+    """Partitions of n keys in the library's shrinking plan, by walking it from the end."""
+    if n <= 0:
+        return 1
+    left, size, count = -(-n // 64) * 64, small, 0
+    while left > 0:
+        for _ in range(2 if size < big else 1):
+            if left > 0:
+                left -= size
+                count += 1
+        size = min(size * 2, big)
+    return count
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
