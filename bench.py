@@ -136,27 +136,26 @@ class DecodeSetup:
                                 self.part, self.stream)
 
     def capture(self):
+        """Capture one step into a native HIP graph (the library's pa_graph_* calls)."""
         torch = self.torch
         self.step_eager()                    # warm the launch path outside capture
         torch.cuda.synchronize()
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(self.stream):
-            with torch.cuda.graph(self.graph, stream=self.stream):
-                self.step_eager()
+        with self.pa.HipGraph.capture(self.stream) as g:
+            self.step_eager()
+        self.graph = g
         torch.cuda.synchronize()
 
     def time_steps(self, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
-            self.graph.replay()
+            self.graph.replay(self.stream)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(self.stream)
         for _ in range(steps):
-            with torch.cuda.stream(self.stream):
-                self.graph.replay()
+            self.graph.replay(self.stream)
         e1.record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -165,23 +164,21 @@ class DecodeSetup:
     def time_batched_steps(self, n, reps, warmup):
         """Device time per step with n steps captured in one graph (ms)."""
         torch = self.torch
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(self.stream):
-            with torch.cuda.graph(g, stream=self.stream):
-                for _ in range(n):
-                    self.step_eager()
+        with self.pa.HipGraph.capture(self.stream) as g:
+            for _ in range(n):
+                self.step_eager()
         torch.cuda.synchronize()
         for _ in range(warmup):
-            g.replay()
+            g.replay(self.stream)
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(self.stream)
         for _ in range(reps):
-            with torch.cuda.stream(self.stream):
-                g.replay()
+            g.replay(self.stream)
         e1.record(self.stream)
         torch.cuda.synchronize()
+        g.close()
         return e0.elapsed_time(e1) / (reps * n)
 
     def time_eager_steps(self, steps, warmup):

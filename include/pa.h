@@ -60,8 +60,10 @@ typedef enum {
     PA_ERR_UNSUPPORTED = 3, /* valid sizes this build has no kernel for           */
     PA_ERR_WORKSPACE = 4,   /* workspace_bytes smaller than required              */
     PA_ERR_LAUNCH = 5,      /* the HIP runtime reported a launch error            */
-    PA_ERR_SCRATCH = 6      /* the call needs more than the library's fixed device
+    PA_ERR_SCRATCH = 6,     /* the call needs more than the library's fixed device
                                scratch (pa_decode_noalloc)                       */
+    PA_ERR_GRAPH = 7        /* the HIP runtime refused a graph capture,
+                               instantiation or launch (pa_graph_*)              */
 } pa_status;
 
 /* Static, NUL-terminated description of a status code (never NULL). */
@@ -413,6 +415,42 @@ int pa_bm_append(pa_block_manager *bm, const int32_t *tokens, int32_t num_tokens
  * become free (most recent last).  PA_ERR_SHAPE for an id out of range or not
  * held; entries before it in reverse order may already have been released. */
 int pa_bm_free(pa_block_manager *bm, const int32_t *block_table, int32_t num_blocks);
+
+/*
+ * Native HIP graphs of library calls, for a serving loop that replays the same
+ * step with new values: the decode step is captured once and replayed, so a step
+ * costs one graph launch instead of one host launch per kernel ([Course] "THE
+ * IMPORTANT DETAILS" item 03: the decode loop runs under a captured graph;
+ * [Atlas] ch.26 captions: a replay reads new values from the same preallocated
+ * buffers, whose addresses and shapes the capture fixed).
+ *
+ * pa_graph_begin(stream) starts capturing the work issued on `stream`
+ * (hipStreamBeginCapture, thread-local mode): calls on that stream from this
+ * thread until pa_graph_end are recorded, not run.  Every device entry point of
+ * this library can be captured (none allocates, synchronises or clears memory
+ * with a memset node).  pa_graph_end(stream, &graph) ends the capture and
+ * instantiates the result into *graph, an opaque handle the caller owns and
+ * releases with pa_graph_destroy.  pa_graph_launch(graph, stream) enqueues one
+ * replay on `stream`: the captured kernels run again with the captured pointers
+ * and sizes, reading whatever the buffers hold when they run, in stream order with
+ * the caller's other work on that stream.  A graph may be launched any number of
+ * times, but replays that share buffers (a workspace in particular) must not
+ * overlap in time: launch them on one stream.  pa_graph_node_counts reports what
+ * was captured: *kernels receives the number of kernel nodes and *others the
+ * number of nodes of any other kind.
+ *
+ * stream   a created stream (not the NULL stream)
+ * Errors: PA_ERR_NULL (NULL stream, graph or out-pointer), PA_ERR_GRAPH (the
+ * runtime refused the capture, the instantiation or the launch).  pa_graph_end
+ * always ends the capture; on failure *graph is set to NULL.
+ */
+typedef struct pa_graph pa_graph;
+
+int pa_graph_begin(hipStream_t stream);
+int pa_graph_end(hipStream_t stream, pa_graph **graph);
+int pa_graph_launch(const pa_graph *graph, hipStream_t stream);
+int pa_graph_node_counts(const pa_graph *graph, size_t *kernels, size_t *others);
+void pa_graph_destroy(pa_graph *graph);
 
 #ifdef __cplusplus
 }

@@ -13,7 +13,8 @@ from .binding import (PaError, library_path, load, pa_decode, pa_decode_workspac
                       pa_decode_store, BlockManager, pa_bm_create, pa_bm_destroy,
                       pa_bm_num_free, pa_bm_ref_count, pa_bm_blocks_needed, pa_bm_allocate,
                       pa_bm_append, pa_bm_free, pa_kv_pool_layout, alloc_kv_pools,
-                      pa_decode_noalloc, NOALLOC_SCRATCH_BYTES)
+                      pa_decode_noalloc, NOALLOC_SCRATCH_BYTES, HipGraph, pa_graph_begin,
+                      pa_graph_end, pa_graph_launch, pa_graph_node_counts, pa_graph_destroy)
 
 __all__ = ["PaError", "library_path", "load", "pa_store_kv", "pa_prefill_varlen",
            "pa_prefill_workspace_size", "pa_prefill_workspace", "pa_decode",
@@ -22,4 +23,5 @@ __all__ = ["PaError", "library_path", "load", "pa_store_kv", "pa_prefill_varlen"
            "pa_status_string", "BlockManager", "pa_bm_create", "pa_bm_destroy",
            "pa_bm_num_free", "pa_bm_ref_count", "pa_bm_blocks_needed", "pa_bm_allocate",
            "pa_bm_append", "pa_bm_free", "pa_kv_pool_layout", "alloc_kv_pools",
-           "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES"]
+           "pa_decode_noalloc", "NOALLOC_SCRATCH_BYTES", "HipGraph", "pa_graph_begin",
+           "pa_graph_end", "pa_graph_launch", "pa_graph_node_counts", "pa_graph_destroy"]

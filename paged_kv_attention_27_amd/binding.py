@@ -76,6 +76,17 @@ def load():
     lib.pa_decode_store.restype = ctypes.c_int
     lib.pa_decode_store.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I,
                                     _I, ctypes.c_float, _I, _P, _SZ, _P, _P]
+    lib.pa_graph_begin.restype = ctypes.c_int
+    lib.pa_graph_begin.argtypes = [_P]
+    lib.pa_graph_end.restype = ctypes.c_int
+    lib.pa_graph_end.argtypes = [_P, ctypes.POINTER(ctypes.c_void_p)]
+    lib.pa_graph_launch.restype = ctypes.c_int
+    lib.pa_graph_launch.argtypes = [_P, _P]
+    lib.pa_graph_node_counts.restype = ctypes.c_int
+    lib.pa_graph_node_counts.argtypes = [_P, ctypes.POINTER(ctypes.c_size_t),
+                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.pa_graph_destroy.restype = None
+    lib.pa_graph_destroy.argtypes = [_P]
     _bind_block_manager(lib)
     _LIB = lib
     return lib
@@ -144,6 +155,88 @@ def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def pa_graph_begin(stream):
+    """Start capturing the library calls issued on `stream` (a torch.cuda.Stream that
+    is not the NULL stream)."""
+    _check("pa_graph_begin", load().pa_graph_begin(_stream(stream)))
+
+
+def pa_graph_end(stream):
+    """End the capture on `stream`; returns the instantiated graph handle (an int)."""
+    h = ctypes.c_void_p()
+    _check("pa_graph_end", load().pa_graph_end(_stream(stream), ctypes.byref(h)))
+    return h.value
+
+
+def pa_graph_launch(graph, stream):
+    _check("pa_graph_launch", load().pa_graph_launch(ctypes.c_void_p(graph), _stream(stream)))
+
+
+def pa_graph_node_counts(graph):
+    """(kernel nodes, other nodes) of a captured graph."""
+    k, o = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("pa_graph_node_counts", load().pa_graph_node_counts(ctypes.c_void_p(graph),
+                                                               ctypes.byref(k), ctypes.byref(o)))
+    return k.value, o.value
+
+
+def pa_graph_destroy(graph):
+    load().pa_graph_destroy(ctypes.c_void_p(graph))
+
+
+class HipGraph:
+    """Owner of one pa_graph handle: capture the calls made inside ``with
+    HipGraph.capture(stream) as g:``, then ``g.replay()`` launches them again on the
+    capture stream (or another one).  The handle is released with the object."""
+
+    def __init__(self, handle, stream):
+        self.handle, self.stream = handle, stream
+
+    @classmethod
+    def capture(cls, stream):
+        return _Capture(cls, stream)
+
+    def replay(self, stream=None):
+        pa_graph_launch(self.handle, stream if stream is not None else self.stream)
+
+    def node_counts(self):
+        return pa_graph_node_counts(self.handle)
+
+    def close(self):
+        if self.handle:
+            pa_graph_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:   # interpreter shutdown: the library may be gone
+            pass
+
+
+class _Capture:
+    def __init__(self, cls, stream):
+        self.cls, self.stream, self.graph = cls, stream, None
+
+    def __enter__(self):
+        pa_graph_begin(self.stream)
+        self.graph = self.cls(None, self.stream)
+        return self.graph
+
+    def __exit__(self, exc_type, exc, tb):
+        try:
+            handle = pa_graph_end(self.stream)   # always ends the capture
+        except PaError:
+            if exc_type is None:
+                raise
+            return False
+        if exc_type is not None:
+            pa_graph_destroy(handle)
+            return False
+        self.graph.handle = handle
+        return False
 
 
 def pa_slot_mapping(cu_seqlens_q, seqlens_k, block_tables, block_size):

@@ -19,8 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "block_manager.cpp", "store_kv.hip", "decode.hip", "prefill.hip",
-           "noalloc.hip"]
+SOURCES = ["pa_api.cpp", "block_manager.cpp", "graph.cpp", "store_kv.hip", "decode.hip",
+           "prefill.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = os.environ.get("PA_OFFLOAD_ARCH", "gfx950")
 

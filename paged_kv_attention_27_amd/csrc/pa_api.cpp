@@ -77,6 +77,7 @@ const char *pa_status_string(int status)
     case PA_ERR_WORKSPACE: return "workspace is too small";
     case PA_ERR_LAUNCH: return "kernel launch failed";
     case PA_ERR_SCRATCH: return "the call needs more than the library's fixed device scratch";
+    case PA_ERR_GRAPH: return "the HIP runtime refused a graph capture, instantiation or launch";
     default: return "unknown status";
     }
 }

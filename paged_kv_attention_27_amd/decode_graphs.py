@@ -16,8 +16,9 @@ length 0 and slot -1: the fused kernel writes a zero row for them, stores
 nothing and reads nothing), and the bucket's graph is replayed.  The graph
 holds one library call, ``pa_decode_store`` (store of the new K/V rows and
 paged attention, plus the reduce pass when contexts are split), so every
-kernel in it comes from libpa; the copies and padding fills run outside the
-graph on the same stream.
+kernel in it comes from libpa; the capture, instantiation and replay are the
+library's own (pa_graph_*, plain HIP graph calls); the copies and padding fills
+run outside the graph on the same stream.
 """
 from __future__ import annotations
 
@@ -75,10 +76,8 @@ class DecodeGraphs:
             self._launch(b)                      # warm the launch path outside capture
         torch.cuda.synchronize()
         for b in self.buckets:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.stream(self.stream):
-                with torch.cuda.graph(g, stream=self.stream):
-                    self._launch(b)
+            with binding.HipGraph.capture(self.stream) as g:
+                self._launch(b)
             self.graphs[b] = g
         torch.cuda.synchronize()
 
@@ -107,6 +106,6 @@ class DecodeGraphs:
             if S < b:                            # padding rows: empty context, no store
                 self.slots[S:b].fill_(-1)
                 self.ctx[S:b].fill_(0)
-            self.graphs[b].replay()
+            self.graphs[b].replay(self.stream)
         torch.cuda.current_stream().wait_stream(self.stream)
         return self.out[:S]

@@ -51,9 +51,22 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(7):
+    for code in range(8):
         assert lib.pa_status_string(code)
     assert b"unknown" in lib.pa_status_string(99)
+
+
+def test_graph_null_arguments(lib):
+    """The graph calls reject NULL streams and handles before touching the runtime."""
+    h = ctypes.c_void_p(0)
+    k, o = ctypes.c_size_t(7), ctypes.c_size_t(7)
+    assert lib.pa_graph_begin(None) == NULL
+    assert lib.pa_graph_end(None, ctypes.byref(h)) == NULL
+    assert lib.pa_graph_launch(None, FAKE) == NULL
+    assert lib.pa_graph_launch(FAKE, None) == NULL
+    assert lib.pa_graph_node_counts(None, ctypes.byref(k), ctypes.byref(o)) == NULL
+    assert lib.pa_graph_node_counts(FAKE, None, ctypes.byref(o)) == NULL
+    lib.pa_graph_destroy(None)   # no-op
 
 
 def test_store_validation(lib):

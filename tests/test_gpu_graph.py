@@ -4,8 +4,10 @@ maxima ("nano-vLLM offline" course, item 03: replay reads new inputs and
 computes new results; "Visual atlas" ch.26: preallocated buffers, values and
 valid lengths may change, the shape/address contract must hold).
 
-Every replay is checked against a fresh oracle run on the same inputs, with
-eager library calls and synchronisations between replays.
+The graphs are the library's own (pa_graph_begin / pa_graph_end /
+pa_graph_launch through the C-ABI); each captured graph is checked to hold
+kernel nodes only.  Every replay is checked against a fresh oracle run on the
+same inputs, with eager library calls and synchronisations between replays.
 """
 import numpy as np
 import pytest
@@ -47,17 +49,19 @@ def test_decode_graph_replays(orc, fused):
     torch.cuda.synchronize()
 
     stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            if fused:
-                pa.pa_decode_store(q_s, k_s, v_s, slots_s, kc, vc, bt, ctx_s, max_ctx, wl.scale,
-                                   workspace=ws, out=out_s, stream=stream)
-            else:
-                pa.pa_store_kv(k_s, v_s, kc, vc, slots_s, stream=stream)
-                pa.pa_decode(q_s, kc, vc, bt, ctx_s, max_ctx, wl.scale, workspace=ws, out=out_s,
-                             stream=stream)
+    with pa.HipGraph.capture(stream) as graph:
+        if fused:
+            pa.pa_decode_store(q_s, k_s, v_s, slots_s, kc, vc, bt, ctx_s, max_ctx, wl.scale,
+                               workspace=ws, out=out_s, stream=stream)
+        else:
+            pa.pa_store_kv(k_s, v_s, kc, vc, slots_s, stream=stream)
+            pa.pa_decode(q_s, kc, vc, bt, ctx_s, max_ctx, wl.scale, workspace=ws, out=out_s,
+                         stream=stream)
     torch.cuda.synchronize()
+    kernels, others = graph.node_counts()
+    n_part = pa.pa_decode_num_partitions(S, Hkv, max_ctx)
+    assert others == 0, "the captured step holds a node that is not a kernel"
+    assert kernels == (0 if fused else 1) + 1 + (n_part > 1), (kernels, n_part)
 
     rng = np.random.default_rng(77)
     for r in range(4):
@@ -178,14 +182,13 @@ def test_prefill_graph_replays(orc, split):
     k_s.zero_(), v_s.zero_(), q_s.zero_()
     torch.cuda.synchronize()
     stream = torch.cuda.Stream()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(stream):
-        with torch.cuda.graph(graph, stream=stream):
-            pa.pa_store_kv(k_s, v_s, kc, vc, slots, stream=stream)
-            pa.pa_prefill_varlen(q_s, None, None, kc, vc, bt, cu_q, cu_k, ph.max_seqlen_q,
-                                 ph.max_seqlen_k, wl.num_kv_heads, wl.scale, out=out_s,
-                                 stream=stream, workspace=ws)
+    with pa.HipGraph.capture(stream) as graph:
+        pa.pa_store_kv(k_s, v_s, kc, vc, slots, stream=stream)
+        pa.pa_prefill_varlen(q_s, None, None, kc, vc, bt, cu_q, cu_k, ph.max_seqlen_q,
+                             ph.max_seqlen_k, wl.num_kv_heads, wl.scale, out=out_s,
+                             stream=stream, workspace=ws)
     torch.cuda.synchronize()
+    assert graph.node_counts() == (2, 0), graph.node_counts()   # store + attention kernels
     rng = np.random.default_rng(42)
     for r in range(3):
         q = workloads.normal_bf16(rng, tuple(q_s.shape), 2.0 if r == 1 else 1.0)
@@ -216,3 +219,31 @@ def test_prefill_graph_replays(orc, split):
         else:
             assert np.array_equal(host_u16(out_s), host_u16(eager)), "replay differs from eager call"
     assert np.array_equal(host_u16(kc), ok) and np.array_equal(host_u16(vc), ov)
+
+
+def test_graph_api_errors():
+    """The capture calls' error paths on a real stream: ending a capture that never
+    began, a failure inside a capture (the capture still ends and the stream works
+    afterwards), and NULL arguments."""
+    import ctypes
+    import paged_kv_attention_27_amd as pa
+    lib = pa.load()
+    stream = torch.cuda.Stream()
+    h = ctypes.c_void_p(123)
+    assert lib.pa_graph_end(ctypes.c_void_p(stream.cuda_stream), ctypes.byref(h)) == 7   # GRAPH
+    assert h.value is None
+    x = torch.zeros(4, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        with pa.HipGraph.capture(stream):
+            raise ValueError("inside the capture")
+    assert lib.pa_graph_launch(None, ctypes.c_void_p(stream.cuda_stream)) == 1          # NULL
+    with torch.cuda.stream(stream):
+        x.add_(1)                           # the stream is out of capture again
+    torch.cuda.synchronize()
+    assert float(x[0]) == 1.0
+    with pa.HipGraph.capture(stream) as g:   # an empty capture instantiates
+        pass
+    assert g.node_counts() == (0, 0)
+    g.replay()
+    torch.cuda.synchronize()
+    g.close()
