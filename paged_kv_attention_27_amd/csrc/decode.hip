@@ -6,7 +6,8 @@
 // Memory-bound split-K design for gfx950:
 //   * one workgroup per (KV head, sequence, partition); the partition plan (the
 //     keys each partition covers, pa_common.h) and the grid order that spreads
-//     the work over the eight XCDs are in locate_partition.  The g = Hq/Hkv
+//     the work over the eight XCDs are in sequence_of_block and
+//     partition_of_block.  The g = Hq/Hkv
 //     query heads of the group share every K/V row the workgroup loads (GQA
 //     without a physical repeat, "Visual atlas" ch.18).
 //   * decode_split_kernel (groups of 1, 2, 4): a token's 256-byte K row is read
@@ -87,28 +88,51 @@ __device__ __forceinline__ void row16_sum_all(float *v)
 // row is the slowest dimension (XCD = (kvh + Hkv y + Hkv S z) mod 8 spreads every
 // row over all XCDs), and the sequence of a row is rotated by the row index so that
 // a sequence's partitions visit different XCDs (a fixed (sequence, head) -> XCD map
-// left the XCDs 10-15 % apart on ragged lengths).  With shrinking partitions, row z
-// holds partition p = z - (n_part - n_s) of a sequence with n_s of them, so the last
-// rows launched are every sequence's small tail.  Returns false if the sequence has
-// no partition in this row.
-__device__ __forceinline__ bool locate_partition(const DecodeArgs &a, int &s, int &p, int &ctx,
-                                                 int &n_s)
+// left the XCDs 10-15 % apart on ragged lengths).  The sequence follows from the
+// grid position alone, so a workgroup can load its queries before its context
+// length arrives.
+__device__ __forceinline__ int sequence_of_block(const DecodeArgs &a)
 {
-    const uint32_t z = blockIdx.z;
-    s = (int)((blockIdx.y + (uint32_t)a.seq_rot * z) % (uint32_t)a.num_seqs);
-    ctx = a.context_lens[s];
+    return (int)((blockIdx.y + (uint32_t)a.seq_rot * blockIdx.z) % (uint32_t)a.num_seqs);
+}
+
+// With shrinking partitions, row z holds partition p = z - (n_part - n_s) of a
+// sequence with n_s of them, so the last rows launched are every sequence's small
+// tail.  Returns false if the sequence has no partition in this row.
+__device__ __forceinline__ bool partition_of_block(const DecodeArgs &a, int ctx, int &p, int &n_s)
+{
+    const int z = (int)blockIdx.z;
     n_s = plan_count(ctx, a.part_tokens, a.part_min);
-    p = a.part_min ? (int)z - (a.n_part - n_s) : (int)z;
+    p = a.part_min ? z - (a.n_part - n_s) : z;
     return p >= 0 && p < n_s;
 }
 
 template <int G, int U, bool CHUNK_IN_BLOCK, bool FUSED_STORE>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 {
-    int s, p, ctx, n_part_s, t_begin, t_end;
-    if (!locate_partition(a, s, p, ctx, n_part_s))
-        return;
+    const int s = sequence_of_block(a);
     const int kvh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int r = lane >> 4;   // lane group: which of the four rows a load instruction covers
+    const int c = lane & 15;   // 8-element slice of the head dimension
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+
+    // q in the dot-product layout: lane c of every lane group holds q[8c .. 8c+8)
+    // (issued first: the loads overlap the context-length load)
+    const bf16 *q = static_cast<const bf16 *>(a.q);
+    uint32_t qw[G][4];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)s * Hq + kvh * G + h) * D + 8 * c);
+        qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
+    }
+
+    const int ctx = a.context_lens[s];
+    int p, n_part_s, t_begin, t_end;
+    if (!partition_of_block(a, ctx, p, n_part_s))
+        return;
     if (ctx <= 0) {   // empty context: a zero output row, defined by the C-ABI
         uint16_t *out = static_cast<uint16_t *>(a.out) + ((int64_t)s * a.num_q_heads + kvh * G) * D;
         for (int i = threadIdx.x; i < G * D; i += kThreads)
@@ -123,29 +147,13 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
         new_slot = a.slot_mapping[s];
     const int t_stop = new_slot >= 0 ? ctx - 1 : t_end;   // keys read from the pool
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int r = lane >> 4;   // lane group: which of the four rows a load instruction covers
-    const int c = lane & 15;   // 8-element slice of the head dimension
-
     __shared__ float red_m[kWaves][G];
     __shared__ float red_l[kWaves][G];
     __shared__ float red_o[kWaves][G][D];
 
     const int bs = a.block_size, shift = a.bs_shift;
     const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const int64_t row_elems = (int64_t)Hkv * D;
-
-    const bf16 *q = static_cast<const bf16 *>(a.q);
-    // q in the dot-product layout: lane c of every lane group holds q[8c .. 8c+8)
-    uint32_t qw[G][4];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(q + ((int64_t)s * Hq + kvh * G + h) * D + 8 * c);
-        qw[h][0] = v.x; qw[h][1] = v.y; qw[h][2] = v.z; qw[h][3] = v.w;
-    }
 
     float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -454,10 +462,29 @@ template <int G, bool CHUNK_IN_BLOCK, bool FUSED_STORE>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a)
 {
     static_assert(G <= 16, "heads of a group fill the 16 MFMA columns");
-    int s, p, ctx, n_part_s, t_begin, t_end;
-    if (!locate_partition(a, s, p, ctx, n_part_s))
-        return;
+    const int s = sequence_of_block(a);
     const int kvh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: descriptors and M0
+    const int g = lane >> 4;     // 16-lane group
+    const int col = lane & 15;   // head column of the score / output accumulators
+    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+    const bf16 *q = static_cast<const bf16 *>(a.q);
+
+    // B operand of the scores: lane l holds Q[head l%16][32 q4 + 8 (l/16) .. +8]
+    // (issued first: the loads overlap the context-length load)
+    bf16x8 qt[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+        qt[q4] = col < G ? *reinterpret_cast<const bf16x8 *>(q + ((int64_t)s * Hq + kvh * G + col) * D +
+                                                               32 * q4 + 8 * g)
+                         : bf16x8{};
+
+    const int ctx = a.context_lens[s];
+    int p, n_part_s, t_begin, t_end;
+    if (!partition_of_block(a, ctx, p, n_part_s))
+        return;
     if (ctx <= 0) {   // empty context: a zero output row, defined by the C-ABI
         uint16_t *out = static_cast<uint16_t *>(a.out) + ((int64_t)s * a.num_q_heads + kvh * G) * D;
         for (int i = threadIdx.x; i < G * D; i += kThreads)
@@ -470,32 +497,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a)
         new_slot = a.slot_mapping[s];
     const int t_stop = new_slot >= 0 ? ctx - 1 : t_end;   // keys read from the pool
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: descriptors and M0
-    const int g = lane >> 4;     // 16-lane group
-    const int col = lane & 15;   // head column of the score / output accumulators
-
     __shared__ __attribute__((aligned(16))) char vst0[kWaves][kMStageB];
     __shared__ __attribute__((aligned(16))) char vst1[kWaves][kMStageB];
 
     const int bs = a.block_size, shift = a.bs_shift;
     const int32_t *bt_row = a.block_tables + (int64_t)s * a.max_blocks;
-    const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
     const int64_t row_elems = (int64_t)Hkv * D;
     const uint32_t row_bytes = (uint32_t)row_elems * 2;
-    const bf16 *q = static_cast<const bf16 *>(a.q);
     const bf16 *kc = static_cast<const bf16 *>(a.k_cache);
     const bf16 *vc = static_cast<const bf16 *>(a.v_cache);
     const float sl2 = a.scale_log2;
-
-    // B operand of the scores: lane l holds Q[head l%16][32 q4 + 8 (l/16) .. +8]
-    bf16x8 qt[4];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4)
-        qt[q4] = col < G ? *reinterpret_cast<const bf16x8 *>(q + ((int64_t)s * Hq + kvh * G + col) * D +
-                                                               32 * q4 + 8 * g)
-                         : bf16x8{};
 
     // transposing-read offsets within a stage: tile t covers head-dim 16 t .. 16 t + 15;
     // lane i of group g reads row 4 g + i/4 (and 16 rows further), columns 16 t + 4 (i%4) .. +4

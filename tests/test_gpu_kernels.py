@@ -415,6 +415,28 @@ def test_decode_store_fused_mqa(pa, orc, bs, part):
     _fused_case(pa, orc, wl, f"fused MQA bs={bs} partition={part}", partition_size=part)
 
 
+# contexts on and around every boundary of the library's shrinking partitions (from
+# the end of the context rounded up to 64: 256, 256, 512, 512, 1024, 1024, then 2048s)
+PLAN_CTX = [1, 63, 64, 65, 255, 256, 257, 511, 513, 1023, 1025, 1535, 1537, 2559, 2561, 3583,
+            3585, 5631, 5633, 8000]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["decode", "fused"])
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (8, 1)], ids=["g2", "g8"])
+def test_decode_shrinking_partitions(pa, orc, hq, hkv, fused):
+    """The library's own partitioning (partition_size 0) with few (sequence, KV head)
+    pairs: every sequence is split into shrinking partitions whose boundaries these
+    contexts straddle; the reduce pass merges a different number of them per sequence."""
+    wl = _wl(q_lens=[1] * len(PLAN_CTX), k_lens=PLAN_CTX, num_q_heads=hq, num_kv_heads=hkv,
+             seed=46, q_scale=4.0, v_position=True)
+    assert pa.pa_decode_num_partitions(len(PLAN_CTX), hkv, max(PLAN_CTX)) > 6, "not split"
+    label = f"shrinking partitions Hq={hq} Hkv={hkv}"
+    if fused:
+        _fused_case(pa, orc, wl, "fused " + label)
+    else:
+        _check(pa, orc, wl, label, decode_too=True)
+
+
 def test_decode_store_fused_negative_slot_reads_pool(pa, orc):
     """A negative slot skips the fused store; the token already in the pool is used."""
     wl = _wl(q_lens=[1] * 4, k_lens=[5, 257, 1000, 64], seed=44, q_scale=3.0)
