@@ -714,6 +714,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a)
 
 constexpr int kReduceThreads = 256;   // two Q heads of one sequence per workgroup
 constexpr int kReduceStage = 512;     // partitions staged in LDS per pass
+constexpr int kReduceRegParts = 32;   // up to this many partitions: merged in registers
 
 __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArgs a)
 {
@@ -730,6 +731,35 @@ __global__ __launch_bounds__(kReduceThreads) void decode_reduce_kernel(DecodeArg
     const int64_t base = ((int64_t)s * a.num_q_heads + h) * a.n_part;
     const float2 *ml = reinterpret_cast<const float2 *>(a.ws_ml) + base;
     const float *wo = a.ws_o + base * D + dd;
+
+    if (np <= kReduceRegParts) {
+        // every load issued at once (the (max, sum) pairs are the same for the 128 threads
+        // of a head), then the merge in registers: one memory round trip, no barrier;
+        // the same operations in the same order as the staged path below
+        float2 mlv[kReduceRegParts];
+        float ov[kReduceRegParts];
+#pragma unroll
+        for (int p = 0; p < kReduceRegParts; ++p)
+            if (p < np) {
+                mlv[p] = ml[p];
+                ov[p] = wo[(int64_t)p * D];
+            }
+        float M = kMaxFloor;
+#pragma unroll
+        for (int p = 0; p < kReduceRegParts; ++p)
+            if (p < np) M = fmaxf(M, mlv[p].x);
+        float L = 0.f, o = 0.f;
+#pragma unroll
+        for (int p = 0; p < kReduceRegParts; ++p)
+            if (p < np) {
+                const float w = fast_exp2(mlv[p].x - M);
+                L = fmaf(w, mlv[p].y, L);
+                o = fmaf(w, ov[p], o);
+            }
+        if (active)
+            *out = f32_to_bf16_bits(o / L);
+        return;
+    }
 
     // global max over the partitions: every thread of the head scans a slice, then LDS
     __shared__ float red[2][D];
