@@ -271,6 +271,15 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
                 sacc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[mt][ks], qreg[ks], sacc[mt], 0, 0, 0);
         // all 16 K reads are issued before the first MFMA, so their latencies overlap; the
         // next tile's copies are spread between the MFMAs so their issue never stalls the wave
+        // every V^T operand of the tile is read right after the score MFMAs (into the
+        // registers the K operands free), so the reads land during the softmax and the
+        // weighted-value MFMAs below issue back to back
+        bf16x8 va[4][4];
+#pragma unroll
+        for (int qs = 0; qs < 4; ++qs)
+#pragma unroll
+            for (int mtd = 0; mtd < 4; ++mtd)
+                va[qs][mtd] = read_vt(cur + voff0[mtd] + 16 * ROWB * qs, cur + voff1[mtd] + 16 * ROWB * qs);
         __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -278,6 +287,7 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 32, 0);
 
         const int kbase = kt * BN;
         if (kbase + BN - 1 > wave_min_kmax) {
@@ -323,13 +333,10 @@ __device__ __forceinline__ void attend_block(const PrefillArgs &a, int s, int qb
             }
 
 #pragma unroll
-        for (int qs = 0; qs < 4; ++qs) {
+        for (int qs = 0; qs < 4; ++qs)
 #pragma unroll
-            for (int mtd = 0; mtd < 4; ++mtd) {
-                const bf16x8 va = read_vt(cur + voff0[mtd] + 16 * ROWB * qs, cur + voff1[mtd] + 16 * ROWB * qs);
-                acc_o[mtd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qs], acc_o[mtd], 0, 0, 0);
-            }
-        }
+            for (int mtd = 0; mtd < 4; ++mtd)
+                acc_o[mtd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[qs][mtd], pb[qs], acc_o[mtd], 0, 0, 0);
 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): tile kt+1 has landed (this wave's part)
         __syncthreads();                      // ... and every wave's part; stage ST is free again
