@@ -123,7 +123,7 @@ class DecodeSetup:
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
         self.stream = torch.cuda.Stream()
         self.bytes = decode_kv_bytes(wl, ph.seqlens_k)
-        self.n_part = pa.pa_decode_num_partitions(S, wl.num_kv_heads, self.max_ctx, partition_size)
+        self.n_part = pa.pa_decode_num_partitions(S, Hq, wl.num_kv_heads, self.max_ctx, partition_size)
         torch.cuda.synchronize()
 
     def args(self):

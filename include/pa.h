@@ -212,10 +212,11 @@ int pa_prefill_varlen_ws(const void *q, const void *k, const void *v,
 
 /*
  * Number of key partitions pa_decode splits the longest context into, for
- * the given partition_size (0 = the library's choice for these sizes).
+ * the given partition_size (0 = the library's choice for these sizes, which
+ * depends on the group size num_q_heads / num_kv_heads).
  * Returns 0 for invalid sizes.
  */
-int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads,
+int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size);
 
 /*
@@ -248,7 +249,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * workspace     (device) >= pa_decode_workspace_size(...) bytes, any content
  * out           (device, out) [num_seqs, num_q_heads, head_dim] bf16
  * partition_size  0 (library's choice: one partition per sequence when
- *               num_seqs * num_kv_heads >= 1024; otherwise partitions of at most
+ *               num_seqs * num_kv_heads >= 1024, or >= 4096 when num_q_heads ==
+ *               num_kv_heads; otherwise partitions of at most
  *               2048 keys that shrink toward the end of each sequence: counted
  *               from the end of the context rounded up to 64, 256, 256, 512, 512,
  *               1024, 1024, then 2048 keys, the first partition taking the rest)

@@ -62,7 +62,7 @@ def load():
     lib.pa_prefill_workspace_size.restype = ctypes.c_size_t
     lib.pa_prefill_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     lib.pa_decode_num_partitions.restype = ctypes.c_int32
-    lib.pa_decode_num_partitions.argtypes = [_I, _I, _I, _I]
+    lib.pa_decode_num_partitions.argtypes = [_I, _I, _I, _I, _I]
     lib.pa_decode_workspace_size.restype = ctypes.c_size_t
     lib.pa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I]
     for name in ("pa_decode", "pa_decode_split", "pa_decode_reduce"):
@@ -339,9 +339,10 @@ def pa_prefill_varlen(q, k, v, k_cache, v_cache, block_tables, cu_seqlens_q, cu_
     return out
 
 
-def pa_decode_num_partitions(num_seqs, num_kv_heads, max_context_len, partition_size=0):
-    return int(load().pa_decode_num_partitions(num_seqs, num_kv_heads, max_context_len,
-                                               partition_size))
+def pa_decode_num_partitions(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                             partition_size=0):
+    return int(load().pa_decode_num_partitions(num_seqs, num_q_heads, num_kv_heads,
+                                               max_context_len, partition_size))
 
 
 def pa_decode_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

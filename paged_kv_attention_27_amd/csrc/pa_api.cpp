@@ -14,6 +14,7 @@ namespace {
 constexpr int kHeadDim = 128;
 // library decode partitioning (partition_size == 0); see resolve_partition
 constexpr int64_t kDecodeWholeSequencePairs = 1024;   // (sequence, KV head) pairs that fill the chip
+constexpr int64_t kDecodeWholeSequencePairsMha = 4096;   // the same with one Q head per KV head
 constexpr int32_t kDecodePartMax = 2048;              // keys: the largest partition
 constexpr int32_t kDecodePartMin = 256;               // keys: the last partition of a sequence
 
@@ -42,17 +43,23 @@ struct Plan {
 // partition_size gives fixed partitions of that many keys.  Otherwise, with at
 // least 1024 (sequence, KV head) pairs every sequence is one partition: the grid
 // already fills the chip several times over, and whole-sequence workgroups need no
-// partials or merge pass.  With fewer pairs the keys are split into partitions of
+// partials or merge pass.  One Q head per KV head is the exception up to 4096
+// pairs: its kernel runs three workgroups per CU (two for larger groups), and the
+// shorter tail outweighs the partials and the merge pass (256 ragged contexts at
+// Hq 8 / Hkv 8: 359 -> 343 us per step, while at Hq 16 / Hkv 8 whole sequences
+// stay ahead, 357 against 363-369 us).  With fewer pairs the keys are split into partitions of
 // at most 2048 keys that shrink to 256 toward the end of each sequence, so the
 // workgroups launched last are short and the chip drains evenly (measured on
 // MI355X against fixed 1024-key partitions: 16 x 32768 keys at Hkv 8 354 -> 343 us,
 // 256 ragged contexts at Hq 8 / Hkv 1 78 -> 65 us).
-Plan resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_kv_heads,
-                       int32_t max_context_len) {
+Plan resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
+                       int32_t num_kv_heads, int32_t max_context_len) {
     if (partition_size != 0)
         return {partition_size, 0};
     const int64_t pairs = (int64_t)num_seqs * num_kv_heads;
-    if (pairs >= kDecodeWholeSequencePairs) {
+    const int64_t whole_at = num_q_heads == num_kv_heads ? kDecodeWholeSequencePairsMha
+                                                         : kDecodeWholeSequencePairs;
+    if (pairs >= whole_at) {
         const int64_t whole = ((int64_t)max_context_len + 255) / 256 * 256;
         return {(int32_t)(whole < 256 ? 256 : whole > (1 << 30) ? (1 << 30) : whole), 0};
     }
@@ -277,13 +284,13 @@ int pa_prefill_varlen_ws(const void *q, const void *k, const void *v, const void
                         workspace_bytes, out, stream);
 }
 
-int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
-                                 int32_t partition_size)
+int32_t pa_decode_num_partitions(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t partition_size)
 {
-    if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0 || partition_size < 0 ||
-        partition_size % 32 != 0)
+    if (num_seqs < 0 || num_q_heads < 1 || num_kv_heads < 1 || max_context_len < 0 ||
+        partition_size < 0 || partition_size % 32 != 0)
         return 0;
-    return num_partitions(max_context_len, resolve_partition(partition_size, num_seqs,
+    return num_partitions(max_context_len, resolve_partition(partition_size, num_seqs, num_q_heads,
                                                              num_kv_heads, max_context_len));
 }
 
@@ -292,8 +299,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
 {
     if (num_q_heads < 1 || head_dim < 1)
         return 0;
-    const int32_t np = pa_decode_num_partitions(num_seqs, num_kv_heads, max_context_len,
-                                                partition_size);
+    const int32_t np = pa_decode_num_partitions(num_seqs, num_q_heads, num_kv_heads,
+                                                max_context_len, partition_size);
     return (size_t)num_seqs * num_q_heads * np * (head_dim + 2) * sizeof(float);
 }
 
@@ -323,7 +330,7 @@ int decode_passes(const void *q, const void *k_cache, const void *v_cache,
         return PA_ERR_UNSUPPORTED;
     if (num_seqs == 0)
         return PA_OK;
-    const Plan part = resolve_partition(partition_size, num_seqs, num_kv_heads,
+    const Plan part = resolve_partition(partition_size, num_seqs, num_q_heads, num_kv_heads,
                                         max_context_len);
     if (num_partitions(max_context_len, part) > 65535)
         return PA_ERR_UNSUPPORTED;   // partitions are a grid dimension

@@ -211,26 +211,29 @@ def test_decode_store_validation(lib):
 
 
 def test_decode_sizes(lib):
-    np_ = lib.pa_decode_num_partitions
-    assert np_(256, 8, 4096, 512) == 8
-    assert np_(256, 8, 4097, 512) == 9
-    assert np_(16, 8, 32768, 1024) == 32
-    assert np_(4, 8, 0, 512) == 1
-    assert np_(4, 8, 100, 33) == 0
+    np_ = lib.pa_decode_num_partitions     # (num_seqs, num_q_heads, num_kv_heads, max_ctx, part)
+    assert np_(256, 16, 8, 4096, 512) == 8
+    assert np_(256, 16, 8, 4097, 512) == 9
+    assert np_(16, 32, 8, 32768, 1024) == 32
+    assert np_(4, 16, 8, 0, 512) == 1
+    assert np_(4, 16, 8, 100, 33) == 0
+    assert np_(4, 0, 8, 100, 0) == 0
     assert lib.pa_decode_workspace_size(3, 16, 8, 128, 1000, 256) == 3 * 16 * 4 * 130 * 4
-    assert np_(256, 8, 4096, 0) == 1      # auto: 2048 pairs fill the chip, one partition
-    assert np_(256, 4, 4096, 0) == 1      # auto: 1024 pairs, one partition
+    assert np_(256, 16, 8, 4096, 0) == 1   # auto: 2048 pairs fill the chip, one partition
+    assert np_(256, 8, 4, 4096, 0) == 1    # auto: 1024 pairs, one partition
+    assert np_(512, 8, 8, 4096, 0) == 1    # auto, one Q head per KV head: 4096 pairs, whole
+    assert np_(256, 8, 8, 4096, 0) == 7    # ... 2048 pairs: still split (three workgroups per CU)
     # auto, fewer pairs: partitions of 2048 keys shrinking to 256 at the end of each
     # sequence (from the end: 256, 256, 512, 512, 1024, 1024, then 2048s)
-    assert np_(256, 2, 4096, 0) == 7      # 4096 = 512 + 3584
-    assert np_(256, 1, 4096, 0) == 7
-    assert np_(16, 8, 32768, 0) == 21     # 15 partitions up to the 3584-key tail, then 6
-    assert np_(4, 8, 1024, 0) == 3        # 1024 = 512 + 256 + 256
-    assert np_(4, 8, 100, 0) == 1         # rounded up to 128: one partition
-    assert np_(1, 1, 3000, 0) == 6        # 3008 (rounded to 64) = 448 + 2560
-    assert np_(1, 8, 10**6, 0) == 493
+    assert np_(256, 8, 2, 4096, 0) == 7    # 4096 = 512 + 3584
+    assert np_(256, 8, 1, 4096, 0) == 7
+    assert np_(16, 32, 8, 32768, 0) == 21  # 15 partitions up to the 3584-key tail, then 6
+    assert np_(4, 16, 8, 1024, 0) == 3     # 1024 = 512 + 256 + 256
+    assert np_(4, 16, 8, 100, 0) == 1      # rounded up to 128: one partition
+    assert np_(1, 8, 1, 3000, 0) == 6      # 3008 (rounded to 64) = 448 + 2560
+    assert np_(1, 16, 8, 10**6, 0) == 493
     for n in list(range(0, 9000, 7)) + [10**5 + 3, 2**20]:
-        assert np_(1, 1, n, 0) == _shrinking_count(n, 2048, 256), n
+        assert np_(1, 8, 1, n, 0) == _shrinking_count(n, 2048, 256), n
 
 
 def _shrinking_count(n, big, small):

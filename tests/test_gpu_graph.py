@@ -59,7 +59,7 @@ def test_decode_graph_replays(orc, fused):
                          stream=stream)
     torch.cuda.synchronize()
     kernels, others = graph.node_counts()
-    n_part = pa.pa_decode_num_partitions(S, Hkv, max_ctx)
+    n_part = pa.pa_decode_num_partitions(S, Hq, Hkv, max_ctx)
     assert others == 0, "the captured step holds a node that is not a kernel"
     assert kernels == (0 if fused else 1) + 1 + (n_part > 1), (kernels, n_part)
 

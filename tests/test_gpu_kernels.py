@@ -429,7 +429,7 @@ def test_decode_shrinking_partitions(pa, orc, hq, hkv, fused):
     contexts straddle; the reduce pass merges a different number of them per sequence."""
     wl = _wl(q_lens=[1] * len(PLAN_CTX), k_lens=PLAN_CTX, num_q_heads=hq, num_kv_heads=hkv,
              seed=46, q_scale=4.0, v_position=True)
-    assert pa.pa_decode_num_partitions(len(PLAN_CTX), hkv, max(PLAN_CTX)) > 6, "not split"
+    assert pa.pa_decode_num_partitions(len(PLAN_CTX), hq, hkv, max(PLAN_CTX)) > 6, "not split"
     label = f"shrinking partitions Hq={hq} Hkv={hkv}"
     if fused:
         _fused_case(pa, orc, wl, "fused " + label)

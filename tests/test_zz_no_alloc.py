@@ -65,7 +65,7 @@ def test_noalloc_matches_decode_twice(pa, orc):
         d, ref = _decode_problem(pa, orc, ctx, hq, hkv, seed)
         need = pa.pa_decode_workspace_size(len(ctx), hq, hkv, 128, max(ctx), part)
         assert 0 < need <= pa.NOALLOC_SCRATCH_BYTES
-        assert pa.pa_decode_num_partitions(len(ctx), hkv, max(ctx), part) > 1
+        assert pa.pa_decode_num_partitions(len(ctx), hq, hkv, max(ctx), part) > 1
         out_ws, out_na = _both(pa, d, part)
         assert torch.equal(out_ws.view(torch.int16), out_na.view(torch.int16)), \
             "pa_decode_noalloc differs from pa_decode"
