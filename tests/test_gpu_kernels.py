@@ -144,6 +144,25 @@ def test_prefill_group_sizes(pa, orc, hq, hkv):
     _check(pa, orc, wl, f"Hq={hq} Hkv={hkv}")
 
 
+@pytest.mark.parametrize("bs", [1, 2, 16, 64, 256, 768])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (32, 8), (8, 1)], ids=["g1", "g2", "g4", "g8"])
+def test_prefill_long_keys(pa, orc, hq, hkv, bs):
+    """Few query blocks over more than 16 key tiles take the eight-wave form, whose
+    two groups of waves split each block's key tiles even/odd: odd and even tile
+    counts, a block past its sequence's end, single rows, long cached prefixes, and
+    every paging mode (per-row tables, per-tile tables, flat keys)."""
+    q = [1, 65, 200, 33]
+    k = [1100, 1200, 1500, 2049]
+    wl = _wl(q_lens=q, k_lens=k, num_q_heads=hq, num_kv_heads=hkv, block_size=bs, seed=31)
+    g = hq // hkv
+    assert -(-max(q) // (128 // g)) * len(q) * hkv <= 256 and max(k) > 1024
+    _check(pa, orc, wl, f"long keys Hq={hq} Hkv={hkv} bs={bs}")
+    if bs == 256:
+        wl = _wl(q_lens=[1100, 1300], k_lens=[1100, 1300], num_q_heads=hq, num_kv_heads=hkv,
+                 paged=False, seed=32)
+        _check(pa, orc, wl, f"long keys flat Hq={hq} Hkv={hkv}")
+
+
 def test_prefill_peaky_positions(pa, orc):
     """q x 8 and position-coded values: a one-key mask shift moves outputs by ~1/16."""
     q = [40, 97, 128, 3]
