@@ -163,6 +163,17 @@ def test_prefill_long_keys(pa, orc, hq, hkv, bs):
         _check(pa, orc, wl, f"long keys flat Hq={hq} Hkv={hkv}")
 
 
+@pytest.mark.parametrize("hq,hkv,bs", [(16, 8, 256), (8, 1, 16)], ids=["g2-tile", "g8-row"])
+def test_prefill_long_keys_empty_chunks(pa, orc, hq, hkv, bs):
+    """The eight-wave form with zero-length chunks in the batch (their workgroups
+    leave before any barrier), a one-row chunk, and peaky position-coded inputs."""
+    q = [0, 40, 0, 1]
+    k = [2000, 1500, 1300, 1100]
+    wl = _wl(q_lens=q, k_lens=k, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
+             q_scale=8.0, v_position=True, seed=33)
+    _check(pa, orc, wl, f"long keys, empty chunks Hq={hq} Hkv={hkv} bs={bs}")
+
+
 def test_prefill_peaky_positions(pa, orc):
     """q x 8 and position-coded values: a one-key mask shift moves outputs by ~1/16."""
     q = [40, 97, 128, 3]
