@@ -145,6 +145,15 @@ class DecodeSetup:
         self.graph = g
         torch.cuda.synchronize()
 
+    def warm(self, seconds):
+        """Replay the captured step for at least `seconds` of wall time (untimed), so a
+        short step is timed at the clocks a busy GPU runs at."""
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                self.graph.replay(self.stream)
+            self.torch.cuda.synchronize()
+
     def time_steps(self, steps, warmup):
         torch = self.torch
         for _ in range(warmup):
@@ -529,18 +538,15 @@ def main():
         ls.capture()
         l_ms, _ = ls.time_steps(max(args.steps // 2, 5), args.warmup)
         _, l_split, l_reduce, _ = ls.time_kernels(max(args.steps // 2, 5))
-        result["decode_long"] = {
+        long_decode = {
             "workload": "16 seqs x 32768 ctx, Hq32/Hkv8/d128, block 256, 2048-block pool",
             "value": round(ls.bytes / (l_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
             "ms_per_step": round(l_ms, 5), "num_partitions": ls.n_part,
             "split_GBs": round(ls.bytes / (l_split * 1e-3) / 1e9, 2),
             "ms_split": round(float(l_split), 5), "ms_reduce": round(float(l_reduce), 5)}
+        result["decode_long"] = long_decode
         log(f"long decode: {l_ms * 1e3:.1f} us/step, split {l_split * 1e3:.1f} us")
         del ls
-        if not args.no_cpu_baseline:
-            log("timing the CPU oracle on the long decode")
-            result["decode_long"]["cpu_baseline"] = cpu_baseline(lwl, args.cpu_budget)
-        del lwl
         torch.cuda.empty_cache()
 
         # MHA / GQA / MQA at 8 Q heads: KV bytes 8:2:1 for the same lengths
@@ -549,21 +555,33 @@ def main():
             hwl = workloads.head_ratio_decode(hkv)
             hs = DecodeSetup(torch, pa, hwl, args.partition)
             hs.capture()
-            h_ms, _ = hs.time_steps(max(args.steps // 2, 5), args.warmup)
-            # the same step launched directly, back to back (no graph-replay gap)
-            d_ms = hs.time_eager_steps(max(args.steps // 2, 5), args.warmup)
+            # these steps are 65-350 us: 50 ms of untimed replays first, then at least
+            # 50 timed ones, so a clock or host transient does not decide the average
+            hs.warm(0.05)
+            h_ms, _ = hs.time_steps(max(args.steps, 50), args.warmup)
+            # the same step launched directly, back to back
+            d_ms = hs.time_eager_steps(max(args.steps, 50), args.warmup)
+            # device time per step with 10 steps captured in one graph (no per-replay
+            # launch gap between steps)
+            b_ms = hs.time_batched_steps(10, max(args.steps // 10, 5), args.warmup)
             ratios[hwl.name] = {"num_kv_heads": hkv, "kv_bytes": hs.bytes,
                                 "ms_per_step": round(h_ms, 5), "num_partitions": hs.n_part,
                                 "value": round(hs.bytes / (h_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
                                 "ms_per_step_direct_launches": round(d_ms, 5),
-                                "value_direct_launches": round(hs.bytes / (d_ms * 1e-3) / 1e9, 2)}
-            log(f"Hq8/Hkv{hkv}: {h_ms * 1e3:.1f} us/step ({d_ms * 1e3:.1f} launched directly), "
-                f"{hs.bytes / (h_ms * 1e-3) / 1e9:.0f} GB/s")
+                                "value_direct_launches": round(hs.bytes / (d_ms * 1e-3) / 1e9, 2),
+                                "ms_per_step_10_per_graph": round(b_ms, 5),
+                                "value_10_per_graph": round(hs.bytes / (b_ms * 1e-3) / 1e9, 2)}
+            log(f"Hq8/Hkv{hkv}: {h_ms * 1e3:.1f} us/step ({d_ms * 1e3:.1f} launched directly, "
+                f"{b_ms * 1e3:.1f} with 10 steps per graph), {hs.bytes / (h_ms * 1e-3) / 1e9:.0f} GB/s")
             del hs, hwl
             torch.cuda.empty_cache()
         result["decode_head_ratios"] = {
             "workload": "256 seqs, ctx U[128,4096], Hq 8 over Hkv 8/2/1, block 256; fused step, HIP graph",
             **ratios}
+        if not args.no_cpu_baseline:   # after the GPU timings: the GPU idles meanwhile
+            log("timing the CPU oracle on the long decode")
+            long_decode["cpu_baseline"] = cpu_baseline(lwl, args.cpu_budget)
+        del lwl
 
         # a short chunk over a long cached prefix: few, long query blocks, where the
         # workspace call splits each block's key range between two workgroups
