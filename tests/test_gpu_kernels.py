@@ -380,11 +380,12 @@ def test_decode_empty_context_gives_zeros(pa):
 
 # ------------------------------------------------------------------ fused store + decode
 
-def _fused_case(pa, orc, wl, label, partition_size=0, skip_store=()):
+def _fused_case(pa, orc, wl, label, partition_size=0, skip_store=(), scale=1.0):
     """pa_decode_store on a one-token-per-sequence problem vs the oracle's store + decode.
 
     Sequences listed in ``skip_store`` get slot -1: their new token is stored
     beforehand with pa_store_kv, so the fused call must read it from the pool.
+    Outputs are compared after dividing both sides by ``scale`` (the value scale).
     """
     ph = wl.prefill
     bs = wl.block_size
@@ -412,8 +413,32 @@ def _fused_case(pa, orc, wl, label, partition_size=0, skip_store=()):
     ref = orc.decode(ph.q, okc, ovc, wl.block_tables, ph.seqlens_k, wl.scale)
     log(f"[{label}]")
     assert np.array_equal(host_u16(kc), okc) and np.array_equal(host_u16(vc), ovc), "pools differ"
-    check_close(host_f64(out), ref, label)
+    check_close(host_f64(out) / scale, ref / scale, label)
     return out
+
+
+@pytest.mark.parametrize("v_scale", [1e30, 1e-6])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 8), (16, 4), (8, 1)], ids=["g1", "g2", "g4", "g8"])
+def test_decode_value_range(pa, orc, hq, hkv, v_scale):
+    """The decode partials, their merge and the fused step keep fp32 state, so
+    they cover the whole range of bf16 values: with |V| around 1e30 and 1e-6
+    every output is finite and matches the oracle after dividing both by the
+    value scale, for every group size (both decode kernels), through the
+    split + reduce passes with 512-key partitions (up to 10 partials per row,
+    merged by the log-sum-exp rule, "Visual atlas" ch.22 captions) and through
+    the fused step on the library's own partition plan."""
+    ctx = [1, 63, 700, 2049, 5000]
+    wl = _wl(q_lens=[1] * len(ctx), k_lens=ctx, num_q_heads=hq, num_kv_heads=hkv, seed=48,
+             q_scale=2.0, v_scale=v_scale)
+    label = f"decode |V| ~ {v_scale:g} Hq={hq} Hkv={hkv}"
+    log(f"[{label}]")
+    g = _gpu_synthetic(pa, wl, decode_too=True, partition_size=512)
+    o = oracle_pipeline(orc, wl)
+    assert np.isfinite(g["decode"]).all() and np.isfinite(g["prefill"]).all()
+    check_close(g["decode"] / v_scale, o["prefill"] / v_scale, label + " split + reduce")
+    check_close(g["prefill"] / v_scale, o["prefill"] / v_scale, label + " prefill")
+    out = _fused_case(pa, orc, wl, label + " fused", scale=v_scale)
+    assert np.isfinite(host_f64(out)).all()
 
 
 @pytest.mark.parametrize("part", [0, 32, 96, 512, 4096])
