@@ -356,6 +356,25 @@ def test_decode_peaky_positions(pa, orc):
     _check(pa, orc, wl, "decode peaky + position values", decode_too=True)
 
 
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (8, 1)], ids=["g2", "g8"])
+def test_hard_max_softmax(pa, orc, hq, hkv):
+    """q x 300: the softmax is a hard maximum (in the log2 domain the top score
+    leads the next by tens), so each output row is essentially the value row of
+    its argmax key.  The running maximum grows many times inside a tile, a
+    partition and across partitions, far beyond the lazy-rescale threshold, and
+    every rescale must keep the state finite and exact.  Decode through split +
+    reduce with 96-key partitions and through the fused step, and a causal
+    prefill over several tiles."""
+    ctx = [1, 65, 700, 2049]
+    wl = _wl(q_lens=[1] * len(ctx), k_lens=ctx, num_q_heads=hq, num_kv_heads=hkv, q_scale=300.0,
+             seed=49)
+    _check(pa, orc, wl, f"hard max decode Hq={hq} Hkv={hkv}", decode_too=True, partition_size=96)
+    _fused_case(pa, orc, wl, f"hard max fused Hq={hq} Hkv={hkv}")
+    wl = _wl(q_lens=[200, 65], k_lens=[700, 65], num_q_heads=hq, num_kv_heads=hkv, q_scale=300.0,
+             seed=50)
+    _check(pa, orc, wl, f"hard max prefill Hq={hq} Hkv={hkv}")
+
+
 def test_decode_single_key_is_exact(pa, orc):
     """One visible key: the output is that value row, exactly, after bf16 rounding."""
     wl = _wl(q_lens=[1, 1, 1], k_lens=[1, 1, 1], seed=25)
