@@ -56,22 +56,6 @@ __device__ __forceinline__ void dpp_add_all(float *v)
                     0, __builtin_bit_cast(int, v[i]), CTRL, 0xF, 0xF, false));
 }
 
-// value of lane h (0..7) of this lane's 16-lane row (DPP row_newbcast); h is a
-// constant once the caller's loop is unrolled
-__device__ __forceinline__ int row_bcast(int v, int h)
-{
-    switch (h) {
-    case 0: return __builtin_amdgcn_update_dpp(0, v, 0x150, 0xF, 0xF, false);
-    case 1: return __builtin_amdgcn_update_dpp(0, v, 0x151, 0xF, 0xF, false);
-    case 2: return __builtin_amdgcn_update_dpp(0, v, 0x152, 0xF, 0xF, false);
-    case 3: return __builtin_amdgcn_update_dpp(0, v, 0x153, 0xF, 0xF, false);
-    case 4: return __builtin_amdgcn_update_dpp(0, v, 0x154, 0xF, 0xF, false);
-    case 5: return __builtin_amdgcn_update_dpp(0, v, 0x155, 0xF, 0xF, false);
-    case 6: return __builtin_amdgcn_update_dpp(0, v, 0x156, 0xF, 0xF, false);
-    default: return __builtin_amdgcn_update_dpp(0, v, 0x157, 0xF, 0xF, false);
-    }
-}
-
 // row16_sum of N independent values, one DPP step across all of them at a time
 // (each lane of a 16-lane row ends with the row's bit-identical total)
 template <int N>
