@@ -390,7 +390,12 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeArgs a)
 // values, masked to weight 0).  Each lane keeps the softmax state of one head
 // (lane mod 16); weights are rounded to bf16 for the MFMA and the sum, as in the
 // dot-product kernel.  Partials and outputs have the dot-product kernel's format,
-// so decode_reduce_kernel merges either.
+// so decode_reduce_kernel merges either.  With the steps inside blocks, the
+// block-table entries of the partition's first 64 blocks are read once, one per
+// lane, and each step takes its entry from that register (v_readlane) instead of
+// a scalar load in front of its K/V loads (measured on MI355X: 256 ragged
+// contexts at Hq 8 / Hkv 1, 62.4 -> 61.1 us per step launched directly; the
+// dot-product kernels gained nothing from the same change).
 constexpr int kMStep = 32;                 // keys per wave step
 constexpr int kMStageB = kMStep * 2 * D;   // 8 KB of V rows
 
@@ -405,6 +410,21 @@ __device__ __forceinline__ int vswz(int r) { return 4 * (r & 3) + ((r >> 2) & 3)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, 0x7fffffff, 0x00020000);
+}
+
+// the table entries of blocks lb0 .. lb0 + 63 of a row, one per lane, clamped to
+// blocks lb0 .. lb_last (those that hold the keys read)
+__device__ __forceinline__ int32_t table_window(const int32_t *bt_row, int lb0, int lb_last)
+{
+    const int lane = threadIdx.x & (kWave - 1);
+    return bt_row[lb0 + min(lane, max(lb_last - lb0, 0))];
+}
+
+// entry of block lb (wave-uniform): from the window when it covers lb, else a load
+__device__ __forceinline__ int32_t table_entry(const int32_t *bt_row, int32_t win, int lb0, int lb)
+{
+    const int rel = lb - lb0;
+    return rel < kWave ? __builtin_amdgcn_readlane(win, rel) : __builtin_amdgcn_readfirstlane(bt_row[lb]);
 }
 
 // merge the four waves' (m, l, o) of each head and emit the partition's result:
@@ -443,7 +463,7 @@ __device__ __forceinline__ void emit_partition(const DecodeArgs &a, int s, int k
 }
 
 template <int G, bool CHUNK_IN_BLOCK, bool FUSED_STORE>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a)
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a)
 {
     static_assert(G <= 16, "heads of a group fill the 16 MFMA columns");
     const int s = sequence_of_block(a);
@@ -507,6 +527,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a)
 
     const int n_steps = (t_stop - t_begin + kMStep - 1) / kMStep;
     const int n_mine = n_steps > wave ? (n_steps - wave + kWaves - 1) / kWaves : 0;
+    const int lb0 = shift >= 0 ? (t_begin >> shift) : (t_begin / bs);
+    int32_t win = 0;
+    if (CHUNK_IN_BLOCK && t_stop > t_begin)
+        win = table_window(bt_row, lb0, shift >= 0 ? ((t_stop - 1) >> shift) : ((t_stop - 1) / bs));
 
     // issue step j's K loads (into kf) and V copies (into the stage)
     auto issue = [&](int j, uint4 (&kf)[2][4], char *stage) __attribute__((always_inline)) {
@@ -515,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeArgs a)
         if (CHUNK_IN_BLOCK) {
             // the step's 32 keys are consecutive rows of one block
             const int lb = __builtin_amdgcn_readfirstlane(shift >= 0 ? (cs >> shift) : (cs / bs));
-            const int64_t row0 = (int64_t)__builtin_amdgcn_readfirstlane(bt_row[lb]) * bs + (cs - lb * bs);
+            const int64_t row0 = (int64_t)table_entry(bt_row, win, lb0, lb) * bs + (cs - lb * bs);
             const __amdgpu_buffer_rsrc_t kr = rsrc_of(kc + row0 * row_elems + kvh * D);
             const __amdgpu_buffer_rsrc_t vr = rsrc_of(vc + row0 * row_elems + kvh * D);
 #pragma unroll
