@@ -17,6 +17,7 @@ constexpr int64_t kDecodeWholeSequencePairs = 1024;   // (sequence, KV head) pai
 constexpr int64_t kDecodeWholeSequencePairsMha = 4096;   // the same with one Q head per KV head
 constexpr int32_t kDecodePartMax = 2048;              // keys: the largest partition
 constexpr int32_t kDecodePartMin = 256;               // keys: the last partition of a sequence
+constexpr int32_t kDecodePartMinMfma = 512;           // the same for groups of 8 (MFMA kernel)
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -51,7 +52,11 @@ struct Plan {
 // at most 2048 keys that shrink to 256 toward the end of each sequence, so the
 // workgroups launched last are short and the chip drains evenly (measured on
 // MI355X against fixed 1024-key partitions: 16 x 32768 keys at Hkv 8 354 -> 343 us,
-// 256 ragged contexts at Hq 8 / Hkv 1 78 -> 65 us).
+// 256 ragged contexts at Hq 8 / Hkv 1 78 -> 65 us).  Groups of 8 run the MFMA kernel,
+// whose workgroups cost more to start and less per key, and take 512-key tail
+// partitions (256 ragged contexts at Hq 8 / Hkv 1: 61.1 -> 59.6 us per step launched
+// directly; 1024-key tails 64.7 us; at Hq 8 / Hkv 2, on the dot-product kernel, 512-key
+// tails cost 98.3 -> 100.8 us, so groups up to 4 keep 256).
 Plan resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_q_heads,
                        int32_t num_kv_heads, int32_t max_context_len) {
     if (partition_size != 0)
@@ -63,7 +68,7 @@ Plan resolve_partition(int32_t partition_size, int32_t num_seqs, int32_t num_q_h
         const int64_t whole = ((int64_t)max_context_len + 255) / 256 * 256;
         return {(int32_t)(whole < 256 ? 256 : whole > (1 << 30) ? (1 << 30) : whole), 0};
     }
-    return {kDecodePartMax, kDecodePartMin};
+    return {kDecodePartMax, num_q_heads / num_kv_heads >= 8 ? kDecodePartMinMfma : kDecodePartMin};
 }
 
 int32_t num_partitions(int32_t max_context_len, Plan pl) {
