@@ -251,9 +251,11 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t n
  * partition_size  0 (library's choice: one partition per sequence when
  *               num_seqs * num_kv_heads >= 1024, or >= 4096 when num_q_heads ==
  *               num_kv_heads; otherwise partitions of at most
- *               2048 keys that shrink toward the end of each sequence: counted
+ *               4096 keys that shrink toward the end of each sequence: counted
  *               from the end of the context rounded up to 64, 256, 256, 512, 512,
- *               1024, 1024, then 2048 keys, the first partition taking the rest)
+ *               1024, 1024, 2048, 2048, then 4096 keys, the first partition
+ *               taking the rest; with num_q_heads / num_kv_heads == 8 the
+ *               smallest are 512 keys: 512, 512, 1024, 1024, 2048, 2048, 4096s)
  *               or a multiple of 32: fixed partitions of that many keys
  * Supported: head_dim == 128; num_q_heads / num_kv_heads in {1, 2, 4, 8};
  * num_seqs <= 65535 and at most 65535 partitions (max_context_len /

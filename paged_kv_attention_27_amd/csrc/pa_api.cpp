@@ -15,7 +15,7 @@ constexpr int kHeadDim = 128;
 // library decode partitioning (partition_size == 0); see resolve_partition
 constexpr int64_t kDecodeWholeSequencePairs = 1024;   // (sequence, KV head) pairs that fill the chip
 constexpr int64_t kDecodeWholeSequencePairsMha = 4096;   // the same with one Q head per KV head
-constexpr int32_t kDecodePartMax = 2048;              // keys: the largest partition
+constexpr int32_t kDecodePartMax = 4096;              // keys: the largest partition
 constexpr int32_t kDecodePartMin = 256;               // keys: the last partition of a sequence
 constexpr int32_t kDecodePartMinMfma = 512;           // the same for groups of 8 (MFMA kernel)
 
@@ -49,10 +49,12 @@ struct Plan {
 // shorter tail outweighs the partials and the merge pass (256 ragged contexts at
 // Hq 8 / Hkv 8: 359 -> 343 us per step, while at Hq 16 / Hkv 8 whole sequences
 // stay ahead, 357 against 363-369 us).  With fewer pairs the keys are split into partitions of
-// at most 2048 keys that shrink to 256 toward the end of each sequence, so the
+// at most 4096 keys that shrink to 256 toward the end of each sequence, so the
 // workgroups launched last are short and the chip drains evenly (measured on
 // MI355X against fixed 1024-key partitions: 16 x 32768 keys at Hkv 8 354 -> 343 us,
-// 256 ragged contexts at Hq 8 / Hkv 1 78 -> 65 us).  Groups of 8 run the MFMA kernel,
+// 256 ragged contexts at Hq 8 / Hkv 1 78 -> 65 us; then 2048 -> 4096 for the largest
+// partition: the 16 x 32768 step 342 -> 337 us, 8192 or 16384 340 us, 1024 353 us; the
+// plans differ only for contexts past 5632 keys).  Groups of 8 run the MFMA kernel,
 // whose workgroups cost more to start and less per key, and take 512-key tail
 // partitions (256 ragged contexts at Hq 8 / Hkv 1: 61.1 -> 59.6 us per step launched
 // directly; 1024-key tails 64.7 us; at Hq 8 / Hkv 2, on the dot-product kernel, 512-key

@@ -223,20 +223,20 @@ def test_decode_sizes(lib):
     assert np_(256, 8, 4, 4096, 0) == 1    # auto: 1024 pairs, one partition
     assert np_(512, 8, 8, 4096, 0) == 1    # auto, one Q head per KV head: 4096 pairs, whole
     assert np_(256, 8, 8, 4096, 0) == 7    # ... 2048 pairs: still split (three workgroups per CU)
-    # auto, fewer pairs: partitions of 2048 keys shrinking to 256 at the end of each
-    # sequence (from the end: 256, 256, 512, 512, 1024, 1024, then 2048s); groups of 8
-    # (the MFMA kernel) stop at 512 (from the end: 512, 512, 1024, 1024, then 2048s)
+    # auto, fewer pairs: partitions of 4096 keys shrinking to 256 at the end of each
+    # sequence (from the end: 256, 256, 512, 512, 1024, 1024, 2048, 2048, then 4096s);
+    # groups of 8 (the MFMA kernel) stop at 512 (512, 512, 1024, 1024, 2048, 2048, 4096s)
     assert np_(256, 8, 2, 4096, 0) == 7    # 4096 = 512 + 3584
     assert np_(256, 8, 1, 4096, 0) == 5    # 4096 = 1024 + 3072
-    assert np_(16, 32, 8, 32768, 0) == 21  # 15 partitions up to the 3584-key tail, then 6
+    assert np_(16, 32, 8, 32768, 0) == 15  # 7 partitions up to the 7680-key tail, then 8
     assert np_(4, 16, 8, 1024, 0) == 3     # 1024 = 512 + 256 + 256
     assert np_(4, 16, 8, 100, 0) == 1      # rounded up to 128: one partition
     assert np_(1, 8, 2, 3000, 0) == 6      # 3008 (rounded to 64) = 448 + 2560
     assert np_(1, 8, 1, 3000, 0) == 4      # 3008 = 1984 + 1024 (512, 512 before it)
-    assert np_(1, 16, 8, 10**6, 0) == 493
+    assert np_(1, 16, 8, 10**6, 0) == 251
     for n in list(range(0, 9000, 7)) + [10**5 + 3, 2**20]:
-        assert np_(1, 8, 2, n, 0) == _shrinking_count(n, 2048, 256), n
-        assert np_(1, 8, 1, n, 0) == _shrinking_count(n, 2048, 512), n
+        assert np_(1, 8, 2, n, 0) == _shrinking_count(n, 4096, 256), n
+        assert np_(1, 8, 1, n, 0) == _shrinking_count(n, 4096, 512), n
 
 
 def _shrinking_count(n, big, small):

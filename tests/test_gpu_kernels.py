@@ -490,10 +490,10 @@ def test_decode_store_fused_mqa(pa, orc, bs, part):
 
 
 # contexts on and around every boundary of the library's shrinking partitions (from
-# the end of the context rounded up to 64: 256, 256, 512, 512, 1024, 1024, then 2048s;
-# for groups of 8: 512, 512, 1024, 1024, then 2048s)
+# the end of the context rounded up to 64: 256, 256, 512, 512, 1024, 1024, 2048, 2048,
+# then 4096s; for groups of 8: 512, 512, 1024, 1024, 2048, 2048, then 4096s)
 PLAN_CTX = [1, 63, 64, 65, 255, 256, 257, 511, 513, 1023, 1025, 1535, 1537, 2047, 2049, 2559,
-            2561, 3071, 3073, 3583, 3585, 5119, 5121, 5631, 5633, 7167, 7169, 8000]
+            2561, 3071, 3073, 3583, 3585, 5119, 5121, 5631, 5633, 7167, 7169, 7679, 7681, 9000]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["decode", "fused"])
