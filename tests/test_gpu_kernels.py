@@ -336,14 +336,16 @@ def test_decode_group_sizes(pa, orc, hq, hkv):
     _check(pa, orc, wl, f"decode Hq={hq} Hkv={hkv}", decode_too=True)
 
 
-@pytest.mark.parametrize("bs,part", [(1, 0), (16, 32), (64, 96), (768, 0), (256, 4096)],
-                         ids=["bs1", "bs16-p32", "bs64-p96", "bs768", "bs256-p4096"])
+@pytest.mark.parametrize("bs,part", [(1, 0), (16, 32), (64, 96), (768, 0), (256, 4096), (32, 4096)],
+                         ids=["bs1", "bs16-p32", "bs64-p96", "bs768", "bs256-p4096", "bs32-p4096"])
 @pytest.mark.parametrize("hq,hkv", [(8, 2), (8, 1)], ids=["g4", "g8"])
 def test_decode_large_groups_paging(pa, orc, hq, hkv, bs, part):
     """Groups of 4 and 8 Q heads (dot-product and MFMA score paths) through every
     paging form: per-row table lookups (block sizes below 32), chunks inside one
     block, partitions from one 32-key chunk up, ragged context tails; peaky
-    softmax and value rows that encode their position."""
+    softmax and value rows that encode their position.  With 32-key blocks and
+    4096-key partitions a partition spans up to 128 blocks, past the 64 table
+    entries the MFMA kernel keeps in a register, so its table-load path runs too."""
     wl = _wl(q_lens=[1] * len(CTX), k_lens=CTX, num_q_heads=hq, num_kv_heads=hkv, block_size=bs,
              seed=27, q_scale=4.0, v_position=True)
     _check(pa, orc, wl, f"decode Hq={hq} Hkv={hkv} bs={bs} partition={part}", decode_too=True,
