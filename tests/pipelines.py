@@ -64,6 +64,9 @@ def prefix_tables(wl):
 
 def check_close(gpu, ref, label, max_tol=PARITY_MAX, mean_tol=PARITY_MEAN):
     assert gpu.shape == ref.shape, (gpu.shape, ref.shape)
+    if gpu.size == 0:   # e.g. a prefill whose every chunk is empty
+        log(f"  {label}: empty output, shapes agree")
+        return 0.0, 0.0
     assert np.isfinite(gpu).all(), f"{label}: non-finite GPU output"
     err = np.abs(gpu - ref)
     mx, mean = float(err.max()), float(err.mean())
