@@ -190,7 +190,9 @@ size_t pa_prefill_workspace_size(int32_t num_seqs, int32_t max_seqlen_q, int32_t
  * blocked computation of [Atlas] ch.22 avoid the full score matrix).  Results
  * differ from pa_prefill_varlen only by fp32 rounding (each half's partial
  * O / l, running max and sum are stored in fp32, so every bf16 value range is
- * covered).
+ * covered), and they do not depend on which half finishes second: both halves
+ * enter the merge in their stored form and in key order, so repeated calls
+ * give the same bits.
  *
  * workspace  (device) >= pa_prefill_workspace_size(...) bytes (sized on the
  *            device the call runs on), 16-byte aligned, zero-filled before its

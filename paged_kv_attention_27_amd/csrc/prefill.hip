@@ -1015,10 +1015,14 @@ __device__ __forceinline__ void split_tail(const PrefillArgs &a, const Item &it,
     const uint32_t *other = static_cast<const uint32_t *>(a.ws_part) + (item * 2 + (1 - it.half)) * kWords;
     const float m1o = __uint_as_float(ldc(other + kOWords + (slot * 2 + 0) * 64 + lane));
     const float l1o = __uint_as_float(ldc(other + kOWords + (slot * 2 + 1) * 64 + lane));
-    const float mmo = fmaxf(mm, m1o);
-    const float v0 = fast_exp2(mm - mmo);          // own O is unnormalised
-    const float v1 = l1o * fast_exp2(m1o - mmo);   // the other's is O / l
-    const float inv2 = 1.f / (lsum * v0 + v1);
+    // both halves enter the merge as they are stored (O / l, max, sum) and in key order
+    // (half 0 first), so the result does not depend on which half arrived second
+    const bool h0 = it.half == 0;
+    const float m0 = h0 ? mm : m1o, m1 = h0 ? m1o : mm;
+    const float mmo = fmaxf(m0, m1);
+    const float w0 = (h0 ? lsum : l1o) * fast_exp2(m0 - mmo);
+    const float w1 = (h0 ? l1o : lsum) * fast_exp2(m1 - mmo);
+    const float inv2 = 1.f / (w0 + w1);
     if (tid == 0)   // ready for the next call
         __hip_atomic_store(&a.ws_cnt[item], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (qrow < it.q_len) {
@@ -1032,8 +1036,9 @@ __device__ __forceinline__ void split_tail(const PrefillArgs &a, const Item &it,
                 float ov[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float w = __uint_as_float(ldc(other + (slot * 64 + 16 * mtd + 4 * g4 + e) * 64 + lane));
-                    ov[e] = (o[i][4 * g4 + e] * v0 + w * v1) * inv2;
+                    const float theirs = __uint_as_float(ldc(other + (slot * 64 + 16 * mtd + 4 * g4 + e) * 64 + lane));
+                    const float own = o[i][4 * g4 + e] * inv;   // the bits this half stored
+                    ov[e] = ((h0 ? own : theirs) * w0 + (h0 ? theirs : own) * w1) * inv2;
                 }
                 uint2 pk;
                 pk.x = pack_bf16x2(ov[0], ov[1]);
